@@ -1,0 +1,250 @@
+/*
+ * moe_prefill.h -- C ABI of the MI355X (gfx950) MoE prompt (prefill) FFN layer.
+ *
+ * One call runs one mixture-of-experts FFN layer over a one-chunk prompt, the
+ * prompt path described on the page "prefill: a layer split's idle card streams
+ * a share of a one-chunk prompt's experts" (Strata #663, section "What"):
+ * activations are quantised (Xq), tokens are routed top-k and grouped into a
+ * row table with per-expert group bounds, a grouped Q4 x Q8 GEMM produces the
+ * gate/up projection (GU), SwiGLU gives H, H is requantised (Hq), a second
+ * grouped GEMM gives the down projection (Dm), and the expert rows are
+ * combined back into token rows with the router weights.  Expert weights can
+ * be streamed from pinned host memory into a fixed-slot device pool with
+ * lookahead prefetch, as on the pages "feat: prefetch streamed layers during
+ * compute" (stable-diffusion.cpp #1905, "Summary" and "Effective behavior")
+ * and "feat: pool VRAM for streamed layer" (stable-diffusion.cpp #1906,
+ * "Summary" and the pool-behaviour table).
+ *
+ * Conventions (all entry points):
+ *  - Return 0 (MOE_OK) on success, a negative MOE_E* code otherwise; the
+ *    message of the last failure on a handle is moe_prefill_last_error(h)
+ *    (moe_prefill_last_error(NULL) for failures before a handle exists).
+ *  - Versioned structs (pages #1905/#1906: controls exposed through a versioned
+ *    params struct and additive constructors, existing layouts preserved).
+ *    Every struct starts with uint32_t struct_size = sizeof() as the caller
+ *    compiled it.  A smaller size is accepted: missing trailing fields take
+ *    their defaults (0).  A larger size is accepted only if every byte past
+ *    the fields this library knows is zero; otherwise MOE_EINVAL.
+ *  - Pointers called "device" are HIP device memory on the handle's device
+ *    (e.g. from torch.empty(..., device="cuda")); "host" pointers are ordinary
+ *    CPU memory, "pinned" ones page-locked host memory (hipHostMalloc, or
+ *    torch.empty(..., pin_memory=True)).  The caller owns every buffer it
+ *    passes; the library never frees caller memory.
+ *  - `stream` arguments are a hipStream_t passed as void* (NULL = the null
+ *    stream).  Work is enqueued on it and the call returns before completion;
+ *    the library never calls hipDeviceSynchronize.
+ *  - A handle is not thread-safe; separate handles are independent.
+ *  - Degradations (smaller pool, shallower prefetch, one slot above the
+ *    budget, synchronous fallback) are warnings: the call succeeds and the
+ *    effective values are reported back.  A mandatory resource that cannot be
+ *    had (workspace, the one pool slot) fails clearly with MOE_ENOMEM; there
+ *    is no hidden fallback (page #1906, pool-behaviour table).
+ */
+#ifndef MOE_PREFILL_H
+#define MOE_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_PREFILL_ABI_VERSION 1
+
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* bad argument, dimension or struct */
+    MOE_ENOMEM = -2,        /* workspace or the mandatory pool slot not allocatable */
+    MOE_EHIP = -3,          /* a HIP runtime call failed */
+    MOE_EUNSUPPORTED = -4,  /* device is not gfx950 */
+    MOE_ESTATE = -5,        /* call not valid in the handle's state (e.g. layer >= 0 before a pool) */
+    MOE_ETIMEOUT = -6       /* a bounded host wait expired */
+};
+
+typedef struct moe_prefill moe_prefill_t;
+
+/* ------------------------------------------------------------- creation --- */
+
+typedef struct moe_prefill_params {
+    uint32_t struct_size;
+    int32_t d_model;          /* d: multiple of 64, 64..16384 */
+    int32_t d_ff;             /* f, per expert: multiple of 64, 64..16384 */
+    int32_t n_experts;        /* E: 1..1024 */
+    int32_t top_k;            /* k: 1..min(E, 64) */
+    int32_t max_tokens;       /* largest T any run will use: >= 1, max_tokens*top_k <= 2^21 */
+    int32_t device;           /* HIP device ordinal */
+    int32_t reserved0;
+    void* workspace;          /* NULL: the library allocates; else a caller-lent
+                                 device buffer of >= moe_prefill_workspace_size()
+                                 bytes, 256-byte aligned, owned by the caller and
+                                 valid until moe_prefill_destroy (the page #663
+                                 "What" lends every stage's prompt buffers the
+                                 same way) */
+    uint64_t workspace_bytes; /* size of `workspace` when lent */
+} moe_prefill_params_t;
+
+/* Device bytes of the per-handle workspace (routing tables, Xq, GU, Hq, Dm,
+ * ...) for these dimensions.  Host only.  MOE_EINVAL on bad dimensions. */
+int moe_prefill_workspace_size(const moe_prefill_params_t* p, uint64_t* bytes);
+
+/* Checks the dimensions and the device (gfx950, else MOE_EUNSUPPORTED),
+ * allocates or adopts the workspace, creates the copy stream and events.
+ * On failure *out is NULL. */
+int moe_prefill_create(const moe_prefill_params_t* p, moe_prefill_t** out);
+
+/* Waits for the handle's copy stream, releases the pool, events, streams and
+ * a library-owned workspace.  NULL is a no-op. */
+void moe_prefill_destroy(moe_prefill_t* h);
+
+/* Message of the last failure on h (h may be NULL: the last failure of a call
+ * that had no handle, per thread).  Never NULL; "" after success. */
+const char* moe_prefill_last_error(const moe_prefill_t* h);
+
+/* ---------------------------------------------------------- weight blob --- */
+/*
+ * A layer's weights are one blob: E experts back to back, each
+ * moe_prefill_expert_bytes() long.  Inside an expert: the gate/up matrix
+ * W_gu [2f, d] and the down matrix W_d [d, f], each as Q4 blocks of 32 along
+ * its input dimension (4-bit integers in [-8, 7], one fp16 scale per block),
+ * in a tiled order matched to the GEMM kernel (see moe_prefill_pack_expert).
+ * Host and device layouts are the same, so filling a pool slot is one copy.
+ */
+uint64_t moe_prefill_expert_bytes(int32_t d_model, int32_t d_ff);
+uint64_t moe_prefill_layer_bytes(int32_t d_model, int32_t d_ff, int32_t n_experts);
+
+/* Packs one expert from its canonical arrays into `dst` (host memory,
+ * moe_prefill_expert_bytes() bytes):
+ *   wgu_q [2f][d]    int8 in [-8, 7]; rows [0, f) gate, rows [f, 2f) up
+ *   wgu_s [2f][d/32] fp16 bits, scale of each block of 32 along d
+ *   wd_q  [d][f]     int8 in [-8, 7]
+ *   wd_s  [d][f/32]  fp16 bits
+ * MOE_EINVAL on a bad dimension or a weight outside [-8, 7]. */
+int moe_prefill_pack_expert(int32_t d_model, int32_t d_ff, const int8_t* wgu_q,
+                            const uint16_t* wgu_s, const int8_t* wd_q, const uint16_t* wd_s,
+                            void* dst);
+
+/* ------------------------------------------------------------ one layer --- */
+
+typedef struct moe_layer_io {
+    uint32_t struct_size;
+    int32_t layer;             /* >= 0: weights come from the stream pool (layer
+                                  index of stream_pool_configure); -1: from
+                                  weights_dev */
+    const void* weights_dev;   /* device: a resident layer blob of
+                                  moe_prefill_layer_bytes() bytes (layer == -1) */
+    int32_t n_tokens;          /* T: 0..max_tokens (0 is a no-op) */
+    int32_t reserved0;
+    const float* x;            /* device [T, d] fp32 activations, 16-byte aligned */
+    const float* logits;       /* device [T, E] fp32 router logits, finite */
+    float* y;                  /* device [T, d] fp32 output, overwritten, 16-byte aligned */
+    /* Optional device exports of the intermediate buffers (NULL = skip).
+       Row index r is the position in the row table, grouped by expert. */
+    int32_t* eidx;             /* [T, k]  expert of slot j of token t */
+    float* weights;            /* [T, k]  router weight of that slot */
+    int32_t* counts;           /* [E]     rows routed to each expert */
+    int32_t* bounds;           /* [E+1]   group bounds, bounds[E] = T*k */
+    int32_t* rows;             /* [T*k]   row table: row r holds pair p = t*k + j */
+    int32_t* pos;              /* [T*k]   inverse: pos[p] = r */
+    int8_t* xq;                /* [T, d]  Q8 codes of x */
+    float* dx;                 /* [T, d/32] Q8 scales of x */
+    float* gu;                 /* [T*k, 2f] gate | up */
+    float* h;                  /* [T*k, f]  SwiGLU output (16-byte aligned) */
+    int8_t* hq;                /* [T*k, f]  Q8 codes of h */
+    float* dh;                 /* [T*k, f/32] Q8 scales of h */
+    float* dm;                 /* [T*k, d]  down projection per row */
+} moe_layer_io_t;
+
+/*
+ * Runs one MoE prefill FFN layer on `stream` (see the file comment for the
+ * steps).  For layer >= 0 the weights are taken from the pool: a resident
+ * slot, a prefetched slot (the stream waits for its copy), or -- when the
+ * layer is not in the pool -- a stream-ordered load into a free slot first
+ * (load-then-compute, page #1905 "Summary").  After enqueueing the layer it
+ * queues prefetches of the next prefetch-depth streamed layers on the copy
+ * stream; a prefetch never overwrites the active slot.
+ * Errors: MOE_EINVAL (bad T or pointers), MOE_ESTATE (layer >= 0 with no pool,
+ * or layer out of range), MOE_EHIP.
+ */
+int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io, void* stream);
+
+/* ---------------------------------------------------------- stream pool --- */
+
+typedef struct stream_pool_params {
+    uint32_t struct_size;
+    int32_t n_layers;                /* L; 0 tears the pool down */
+    const void* const* host_blobs;   /* [L] pinned host blobs of layer_bytes each,
+                                        caller-owned, valid until reconfigure/destroy */
+    uint64_t layer_bytes;            /* must equal moe_prefill_layer_bytes() */
+    int32_t prefetch_depth;          /* requested lookahead N >= 0 (0 = load-then-compute) */
+    int32_t resident_layers;         /* max resident leading layers; -1 = as many as the budget leaves */
+    int64_t max_vram_bytes;          /* > 0: budget for the pool; 0: no cap */
+    int32_t requested_slots;         /* > 0: cap on the slot count; 0: derive */
+    /* outputs */
+    int32_t eff_slots;               /* slots allocated (one contiguous allocation) */
+    int32_t eff_depth;               /* effective prefetch depth */
+    int32_t eff_residents;           /* resident leading layers */
+    int32_t warnings;                /* MOE_WARN_* bits */
+    int32_t reserved0;
+} stream_pool_params_t;
+
+#define MOE_WARN_SLOT_OVER_BUDGET 1  /* the one mandatory slot exceeds max_vram_bytes */
+#define MOE_WARN_POOL_DEGRADED    2  /* allocation failed; fewer slots than planned */
+#define MOE_WARN_DEPTH_REDUCED    4  /* prefetch depth reduced to fit */
+
+/*
+ * Plans and allocates the slot pool (pages #1905 "Summary"/"Effective
+ * behavior" and #1906 "Summary"/pool-behaviour table):
+ *  - one slot is mandatory execution memory, tried even above the budget
+ *    (warning); the prefetch window is served before optional residents;
+ *    only residents + 1 + depth slots are allocated, never the whole budget;
+ *  - the pool is one contiguous device allocation of fixed-size slots; on
+ *    allocation failure fewer slots of the same size are tried (residents
+ *    first, then depth) down to one; if one slot fails: MOE_ENOMEM;
+ *  - resident layers are uploaded before returning;
+ *  - calling again first drains the copy stream and releases the previous
+ *    pool, prefetches and residents.
+ * Effective values are written back into *inout.
+ */
+int stream_pool_configure(moe_prefill_t* h, stream_pool_params_t* inout);
+
+/* Pure planning step of stream_pool_configure (no device, no allocation), for
+ * callers that want to see the plan first.  max_alloc_slots simulates the
+ * allocator: > 0 means a pool of more slots than this fails to allocate, -1
+ * means every allocation fails, 0 means none fail. */
+typedef struct moe_pool_plan {
+    uint32_t struct_size;
+    int32_t n_layers;
+    uint64_t slot_bytes;
+    int32_t prefetch_depth;
+    int32_t resident_layers;
+    int64_t max_vram_bytes;
+    int32_t requested_slots;
+    int32_t max_alloc_slots;
+    /* outputs */
+    int32_t slots, depth, residents, warnings;
+} moe_pool_plan_t;
+
+int moe_prefill_plan_pool(moe_pool_plan_t* inout);
+
+/* ---------------------------------------------------------------- stats --- */
+
+typedef struct moe_stats {
+    uint32_t struct_size;
+    int32_t reserved0;
+    uint64_t layers_run;
+    uint64_t prefetch_queued;        /* prefetch copies enqueued */
+    uint64_t prefetch_activated;     /* layers that found their prefetched slot */
+    uint64_t sync_loads;             /* load-then-compute copies */
+    uint64_t prefetch_failed;        /* prefetch enqueues that failed (fell back) */
+    uint64_t bytes_h2d;              /* bytes copied into the pool */
+    int32_t eff_slots, eff_depth, eff_residents, warnings;
+} moe_stats_t;
+
+int moe_prefill_get_stats(const moe_prefill_t* h, moe_stats_t* inout);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_PREFILL_H */

@@ -1,0 +1,57 @@
+// Launch interface of the MoE prefill kernels (host side of moe_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct GemmArgs {
+    const int8_t* A;          // activation codes [rows, K]
+    const float* A_scale;     // their block scales [rows, K/32]
+    const int32_t* row_src;   // grouped row -> A row (nullptr: identity)
+    const uint8_t* blob;      // layer weight blob
+    uint64_t expert_stride;   // bytes per expert
+    uint64_t q_off, s_off;    // matrix quant / scale section offsets in an expert
+    const int32_t* tiles;     // [max_tiles][3]: expert, first row, end row
+    const int32_t* ntiles;    // number of valid tiles (device)
+    float* out;               // [R, N]
+    int N, K;
+    int gu_f;                 // f for the interleaved gate/up matrix, 0 otherwise
+};
+
+struct LayerLaunch {
+    int T, d, f, E, k, W;
+    const float* x;
+    const float* logits;
+    float* y;
+    const uint8_t* blob;
+    uint64_t expert_stride, gu_q_off, gu_s_off, d_q_off, d_s_off;
+    int32_t* eidx;
+    float* wts;
+    uint32_t* mask;
+    int32_t* wprefix;
+    int32_t* counts;
+    int32_t* bounds;
+    int32_t* tiles;
+    int32_t* ntiles;
+    int32_t* rows;
+    int32_t* pos;
+    int32_t* rtok;
+    int8_t* xq;
+    float* dx;
+    float* gu;
+    int8_t* hq;
+    float* dh;
+    float* dm;
+    float* h_out;             // optional export of H (nullptr: not written)
+};
+
+// route, quantise X, group, scatter, GU GEMM, SwiGLU+Q8, down GEMM (last reader
+// of the weights) -- everything up to the combine.
+hipError_t launch_layer(const LayerLaunch& L, hipStream_t st);
+// combine (and clear the membership mask for the next layer)
+hipError_t launch_combine(const LayerLaunch& L, hipStream_t st);
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
+
+}  // namespace moe

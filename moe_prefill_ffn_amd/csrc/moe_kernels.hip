@@ -1,0 +1,616 @@
+// HIP kernels (CDNA4 / gfx950) of the MoE prompt (prefill) FFN layer.
+//
+// The steps follow the prompt path of the page "prefill: a layer split's idle
+// card streams a share of a one-chunk prompt's experts" (Strata #663, section
+// "What"): mixed activations -> Xq, router -> row table + group bounds,
+// GU = grouped GEMM, H = SwiGLU, Hq, Dm = grouped GEMM, combine.  The page
+// names these buffers only; the arithmetic read here is:
+//   route     top-k of the E logits (ties to the lower expert index), weights =
+//             softmax over the k selected logits (fp32)
+//   group     stable counting sort of the pairs p = t*k + j on their expert
+//   Q8        blocks of 32: scale = amax/127 (fp32), code = rint(x/scale) clamped
+//   GEMM      Q4 weights (int4, fp16 scale per 32 along K) x Q8 activations,
+//             exact int32 dot per 32-block on the int8 MFMA, blocks combined in
+//             fp32 in ascending order: acc = fma((float)isum, a_scale*w_scale, acc)
+//   SwiGLU    h = g / (1 + exp(-g)) * u
+//   combine   y[t] = sum_j w[t,j] * Dm[pos(t,j)], j ascending, fma chain
+//
+// Build flags (see build.py): -ffp-contract=off, no fast-math, correctly
+// rounded fp32 division, fp32 denormals kept, packed-fp32 instructions off.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_layout.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------------ exp ---
+// fp32 exponential: Cody-Waite reduction (Cody & Waite, "Software Manual for
+// the Elementary Functions", 1980) with ln2 split into fp32 hi/lo parts, a
+// degree-7 Taylor polynomial (coefficients 1/j! rounded to fp32) in Horner
+// form, and the scale 2^n applied as two exact power-of-two factors.  Each
+// step is a single IEEE operation, so the result is reproducible bit for bit.
+__device__ __forceinline__ float pow2_exact(int n)  // n in [-126, 127]
+{
+    return __int_as_float((n + 127) << 23);
+}
+
+__device__ __forceinline__ float exp_cw(float x)
+{
+    if (x != x) return x;
+    if (x > 89.0f) return __int_as_float(0x7f800000);
+    if (x < -104.0f) return 0.0f;
+    const float n = __builtin_rintf(x * 0x1.715476p+0f);     // x * log2(e)
+    float r = __builtin_fmaf(-n, 0x1.62e430p-1f, x);          // - n * ln2_hi
+    r = __builtin_fmaf(-n, -0x1.05c610p-29f, r);              // - n * ln2_lo
+    float p = 0x1.a01a02p-13f;                                // 1/7!
+    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);                // 1/6!
+    p = __builtin_fmaf(p, r, 0x1.111112p-7f);                 // 1/5!
+    p = __builtin_fmaf(p, r, 0x1.555556p-5f);                 // 1/4!
+    p = __builtin_fmaf(p, r, 0x1.555556p-3f);                 // 1/3!
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    const int ni = (int)n;
+    const int n1 = ni / 2;
+    const int n2 = ni - n1;
+    return (p * pow2_exact(n1)) * pow2_exact(n2);
+}
+
+// Q8 code of v given the block scale d (d > 0): rint(v / d) clamped to +-127.
+__device__ __forceinline__ int q8_code(float v, float d)
+{
+    float q = __builtin_rintf(v / d);
+    q = q > 127.0f ? 127.0f : q;
+    q = q < -127.0f ? -127.0f : q;
+    return (int)q;
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d)
+{
+    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+           ((uint32_t)(d & 0xff) << 24);
+}
+
+// Quantise the 4 values this lane holds of a 32-block spread over 8 lanes
+// (lanes 8g .. 8g+7 of the wave hold one block).  Returns the packed codes;
+// *scale gets the block scale.
+__device__ __forceinline__ uint32_t q8_block_of8(float4 v, float* scale)
+{
+    float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    const float d = m / 127.0f;
+    *scale = d;
+    if (d == 0.0f) return 0u;
+    return pack4(q8_code(v.x, d), q8_code(v.y, d), q8_code(v.z, d), q8_code(v.w, d));
+}
+
+// ---------------------------------------------------------------- route ---
+// One wave per token.  Lane l holds logits l, l+64, ...  Each of the k rounds
+// takes the best remaining (logit, index) pair -- larger logit, then lower
+// index -- by a butterfly over the wave.  Also sets the token's bit in the
+// expert membership mask used by the grouping step.
+__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E,
+                                               int k, int32_t* __restrict__ eidx,
+                                               float* __restrict__ wts, uint32_t* __restrict__ mask,
+                                               int W)
+{
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int nper = (E + 63) >> 6;   // <= 16
+    float v[16];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = lane + 64 * i;
+        if (i < nper && e < E) {
+            v[i] = logits[(int64_t)t * E + e];
+        } else {
+            v[i] = 0.0f;
+            taken |= 1u << i;
+        }
+    }
+    float my_v = 0.0f;
+    int my_i = 0;
+    for (int j = 0; j < k; ++j) {
+        float bv = -__int_as_float(0x7f800000);
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i < nper && !((taken >> i) & 1u)) {
+                const int e = lane + 64 * i;
+                if (v[i] > bv || (v[i] == bv && e < bi)) {
+                    bv = v[i];
+                    bi = e;
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            const float ov = __shfl_xor(bv, m);
+            const int oi = __shfl_xor(bi, m);
+            if (ov > bv || (ov == bv && oi < bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        if (lane == j) {
+            my_v = bv;
+            my_i = bi;
+        }
+    }
+    // softmax over the k selected logits; sum in ascending slot order
+    const float top = __shfl(my_v, 0);
+    const float z = lane < k ? exp_cw(my_v - top) : 0.0f;
+    float s = 0.0f;
+    for (int j = 0; j < k; ++j) s += __shfl(z, j);
+    if (lane < k) {
+        eidx[(int64_t)t * k + lane] = my_i;
+        wts[(int64_t)t * k + lane] = z / s;
+        atomicOr(&mask[(int64_t)my_i * W + (t >> 5)], 1u << (t & 31));
+    }
+}
+
+// ------------------------------------------------------------- quantise ---
+// x is a flat array of n_blocks 32-float blocks (a row-major [rows, K] matrix
+// with K % 32 == 0).  8 lanes per block, 4 values per lane.
+__global__ __launch_bounds__(256) void k_quant_q8(const float* __restrict__ x, int64_t n_blocks,
+                                                  int8_t* __restrict__ q, float* __restrict__ scale)
+{
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t blk = g >> 3;
+    if (blk >= n_blocks) return;          // whole 8-lane groups exit together
+    const int sub = threadIdx.x & 7;
+    const float4 v = *reinterpret_cast<const float4*>(x + blk * 32 + sub * 4);
+    float d;
+    const uint32_t packed = q8_block_of8(v, &d);
+    *reinterpret_cast<uint32_t*>(q + blk * 32 + sub * 4) = packed;
+    if (sub == 0) scale[blk] = d;
+}
+
+// ---------------------------------------------------------- SwiGLU + Q8 ---
+// gu [R, 2f] (gate | up) -> h = silu(gate) * up -> Q8 blocks of 32 along f.
+__global__ __launch_bounds__(256) void k_swiglu_q8(const float* __restrict__ gu, int64_t R, int f,
+                                                   int8_t* __restrict__ hq, float* __restrict__ dh,
+                                                   float* __restrict__ h_out)
+{
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int nbf = f >> 5;
+    const int64_t blk = g >> 3;
+    if (blk >= R * nbf) return;
+    const int sub = threadIdx.x & 7;
+    const int64_t r = blk / nbf;
+    const int b = (int)(blk - r * nbf);
+    const float* gr = gu + r * 2 * f + b * 32 + sub * 4;
+    const float4 gv = *reinterpret_cast<const float4*>(gr);
+    const float4 uv = *reinterpret_cast<const float4*>(gr + f);
+    float4 hv;
+    hv.x = gv.x / (1.0f + exp_cw(-gv.x)) * uv.x;
+    hv.y = gv.y / (1.0f + exp_cw(-gv.y)) * uv.y;
+    hv.z = gv.z / (1.0f + exp_cw(-gv.z)) * uv.z;
+    hv.w = gv.w / (1.0f + exp_cw(-gv.w)) * uv.w;
+    if (h_out) *reinterpret_cast<float4*>(h_out + r * f + b * 32 + sub * 4) = hv;
+    float d;
+    const uint32_t packed = q8_block_of8(hv, &d);
+    *reinterpret_cast<uint32_t*>(hq + r * f + b * 32 + sub * 4) = packed;
+    if (sub == 0) dh[blk] = d;
+}
+
+// ---------------------------------------------------------------- group ---
+// Per expert: exclusive prefix of the membership-mask popcounts over the
+// 32-token words, and the expert's row count.
+__global__ __launch_bounds__(256) void k_group_prefix(const uint32_t* __restrict__ mask, int W,
+                                                      int32_t* __restrict__ wprefix,
+                                                      int32_t* __restrict__ counts)
+{
+    __shared__ int wave_tot[4];
+    const int e = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int running = 0;
+    for (int base = 0; base < W; base += 256) {
+        const int w = base + threadIdx.x;
+        const int c = w < W ? __popc(mask[(int64_t)e * W + w]) : 0;
+        int incl = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        if (lane == 63) wave_tot[wave] = incl;
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            before += i < wave ? wave_tot[i] : 0;
+            total += wave_tot[i];
+        }
+        if (w < W) wprefix[(int64_t)e * W + w] = running + before + incl - c;
+        running += total;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) counts[e] = running;
+}
+
+// One workgroup: group bounds (exclusive scan of counts) and the GEMM row-tile
+// list (expert, first row, end row) in expert order, kBM rows per tile.
+__global__ __launch_bounds__(1024) void k_group_bounds(const int32_t* __restrict__ counts, int E,
+                                                       int32_t* __restrict__ bounds,
+                                                       int32_t* __restrict__ tiles,
+                                                       int32_t* __restrict__ ntiles)
+{
+    __shared__ int tot_c[16], tot_t[16];
+    const int e = threadIdx.x;
+    const int lane = e & 63, wave = e >> 6;
+    const int c = e < E ? counts[e] : 0;
+    const int nt = (c + kBM - 1) / kBM;
+    int ic = c, it = nt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int yc = __shfl_up(ic, o);
+        const int yt = __shfl_up(it, o);
+        if (lane >= o) {
+            ic += yc;
+            it += yt;
+        }
+    }
+    if (lane == 63) {
+        tot_c[wave] = ic;
+        tot_t[wave] = it;
+    }
+    __syncthreads();
+    int bc = 0, bt = 0, all_c = 0, all_t = 0;
+    for (int i = 0; i < 16; ++i) {
+        bc += i < wave ? tot_c[i] : 0;
+        bt += i < wave ? tot_t[i] : 0;
+        all_c += tot_c[i];
+        all_t += tot_t[i];
+    }
+    if (e < E) {
+        const int start = bc + ic - c;
+        const int tstart = bt + it - nt;
+        bounds[e] = start;
+        for (int i = 0; i < nt; ++i) {
+            const int r0 = start + i * kBM;
+            const int r1 = r0 + kBM < start + c ? r0 + kBM : start + c;
+            tiles[3 * (tstart + i) + 0] = e;
+            tiles[3 * (tstart + i) + 1] = r0;
+            tiles[3 * (tstart + i) + 2] = r1;
+        }
+    }
+    if (e == 0) {
+        bounds[E] = all_c;
+        *ntiles = all_t;
+    }
+}
+
+// Row table: pair p = t*k + j goes to row bounds[e] + (number of tokens
+// before t routed to e), read off the membership mask -- a stable order in p.
+__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eidx, int64_t R, int k,
+                                                 const uint32_t* __restrict__ mask,
+                                                 const int32_t* __restrict__ wprefix,
+                                                 const int32_t* __restrict__ bounds, int W,
+                                                 int32_t* __restrict__ rows, int32_t* __restrict__ pos,
+                                                 int32_t* __restrict__ rtok)
+{
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= R) return;
+    const int t = (int)(p / k);
+    const int e = eidx[p];
+    const int64_t wi = (int64_t)e * W + (t >> 5);
+    const uint32_t below = mask[wi] & ((1u << (t & 31)) - 1u);
+    int row = bounds[e] + wprefix[wi] + __popc(below);
+    // a consistent table always gives row in [0, R); the clamp only keeps an
+    // inconsistent one from writing outside the buffers
+    row = row < 0 ? 0 : (row >= (int)R ? (int)R - 1 : row);
+    rows[row] = (int32_t)p;
+    pos[p] = row;
+    rtok[row] = t;
+}
+
+// ---------------------------------------------------------- grouped GEMM ---
+// out[r, n] = sum_b isum(r, n, b) * a_scale[src(r), b] * w_scale[e, n, b]
+// for the rows r of each row tile (all of one expert e).
+//
+// Workgroup = 4 waves = one row tile (64 rows) x 4 weight n-tiles (128 output
+// columns); wave w owns n-tile 4*blockIdx.x + w for all 64 rows (two 32x32
+// MFMA tiles stacked along M, sharing the unpacked B operand).  The gathered
+// A rows and their block scales are staged through LDS 256 K-bytes (8 blocks)
+// at a time, double buffered; each wave streams its own packed Q4 weights
+// straight from global memory (one 16-byte coalesced load per K pair).
+constexpr int kStageK = 256;            // K bytes per LDS stage
+constexpr int kAPitch = kStageK + 16;   // padded LDS row pitch
+
+__device__ __forceinline__ uint32_t nib_to_i8(uint32_t v)   // 4 offset-binary nibbles -> 4 int8
+{
+    return (v + 0x78787878u) ^ 0x80808080u;
+}
+
+__global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs g)
+{
+    const int tile = blockIdx.y;
+    if (tile >= *g.ntiles) return;   // uniform across the workgroup
+    const int e = g.tiles[3 * tile + 0];
+    const int r0 = g.tiles[3 * tile + 1];
+    const int nrows = g.tiles[3 * tile + 2] - r0;   // 1 .. kBM
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = g.K, N = g.N;
+    const int nbk = K >> 5, npairs = K >> 6;
+    const int nt = blockIdx.x * 4 + wave;
+    const bool wave_on = nt < (N >> 5);
+    const int nstages = (K + kStageK - 1) / kStageK;
+
+    __shared__ __attribute__((aligned(16))) int8_t sA[2][kBM * kAPitch];
+    __shared__ __attribute__((aligned(16))) float sS[2][8][kBM];
+
+    // ---- per-thread A fill assignment: 4 x 16 bytes, rows (idx >> 4), col (idx & 15) * 16
+    const int8_t* a_src[4];
+    int a_lds[4], a_col[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = i * 256 + tid;
+        const int row = idx >> 4;
+        const int r = r0 + (row < nrows ? row : 0);
+        const int src = g.row_src ? g.row_src[r] : r;
+        a_src[i] = row < nrows ? g.A + (int64_t)src * K : nullptr;
+        a_col[i] = (idx & 15) * 16;
+        a_lds[i] = row * kAPitch + a_col[i];
+    }
+    // scales fill: thread -> row tid >> 2, blocks 2*(tid & 3) and +1 of the stage
+    const int s_row = tid >> 2, s_b = (tid & 3) * 2;
+    const float* s_src = nullptr;
+    if (s_row < nrows) {
+        const int r = r0 + s_row;
+        const int src = g.row_src ? g.row_src[r] : r;
+        s_src = g.A_scale + (int64_t)src * nbk;
+    }
+
+    // ---- this wave's weight stream
+    const uint8_t* ex = g.blob + (uint64_t)e * g.expert_stride;
+    const uint4* wq = reinterpret_cast<const uint4*>(ex + g.q_off) + (int64_t)nt * npairs * 64 + lane;
+    const uint32_t* ws = reinterpret_cast<const uint32_t*>(ex + g.s_off) + (int64_t)nt * npairs * 32 + (lane & 31);
+
+    uint4 a_reg[4];
+    float2 s_reg;
+    uint4 bq_cur[4], bq_nxt[4];
+    uint32_t bs_cur[4], bs_nxt[4];
+
+    auto load_a = [&](int stage) {
+        const int k0 = stage * kStageK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (a_src[i] && k0 + a_col[i] < K)
+                a_reg[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0 + a_col[i]);
+            else
+                a_reg[i] = make_uint4(0, 0, 0, 0);
+        }
+        const int b0 = stage * 8 + s_b;
+        s_reg.x = (s_src && b0 < nbk) ? s_src[b0] : 0.0f;
+        s_reg.y = (s_src && b0 + 1 < nbk) ? s_src[b0 + 1] : 0.0f;
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sA[buf][a_lds[i]]) = a_reg[i];
+        sS[buf][s_b][s_row] = s_reg.x;
+        sS[buf][s_b + 1][s_row] = s_reg.y;
+    };
+    auto load_b = [&](int stage, uint4* bq, uint32_t* bs) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int pr = stage * 4 + p;
+            if (wave_on && pr < npairs) {
+                bq[p] = wq[(int64_t)pr * 64];
+                bs[p] = ws[(int64_t)pr * 32];
+            } else {
+                bq[p] = make_uint4(0, 0, 0, 0);
+                bs[p] = 0;
+            }
+        }
+    };
+
+    float acc0[16], acc1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        acc0[i] = 0.0f;
+        acc1[i] = 0.0f;
+    }
+    const bool two = nrows > 32;
+    const int h = lane >> 5;
+    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+
+    load_a(0);
+    load_b(0, bq_cur, bs_cur);
+    store_a(0);
+
+    for (int s = 0; s < nstages; ++s) {
+        const int buf = s & 1;
+        __syncthreads();
+        const bool more = s + 1 < nstages;
+        if (more) {
+            load_a(s + 1);
+            load_b(s + 1, bq_nxt, bs_nxt);
+        }
+        if (wave_on) {
+            const int pairs_here = npairs - s * 4 < 4 ? npairs - s * 4 : 4;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                if (p < pairs_here) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int bl = 2 * p + q;
+                        const uint32_t w0 = q ? bq_cur[p].z : bq_cur[p].x;
+                        const uint32_t w1 = q ? bq_cur[p].w : bq_cur[p].y;
+                        v4i bop;
+                        bop.x = (int)nib_to_i8(w0 & 0x0F0F0F0Fu);
+                        bop.y = (int)nib_to_i8((w0 >> 4) & 0x0F0F0F0Fu);
+                        bop.z = (int)nib_to_i8(w1 & 0x0F0F0F0Fu);
+                        bop.w = (int)nib_to_i8((w1 >> 4) & 0x0F0F0F0Fu);
+                        const uint16_t hb = (uint16_t)(q ? (bs_cur[p] >> 16) : (bs_cur[p] & 0xffffu));
+                        const float dw = (float)__builtin_bit_cast(_Float16, hb);
+                        {
+                            const v4i a = *reinterpret_cast<const v4i*>(
+                                &sA[buf][(lane & 31) * kAPitch + bl * 32 + h * 16]);
+                            const v16i is = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop, zero, 0, 0, 0);
+#pragma unroll
+                            for (int gq = 0; gq < 4; ++gq) {
+                                const float4 dx = *reinterpret_cast<const float4*>(&sS[buf][bl][8 * gq + 4 * h]);
+                                acc0[4 * gq + 0] = __builtin_fmaf((float)is[4 * gq + 0], dx.x * dw, acc0[4 * gq + 0]);
+                                acc0[4 * gq + 1] = __builtin_fmaf((float)is[4 * gq + 1], dx.y * dw, acc0[4 * gq + 1]);
+                                acc0[4 * gq + 2] = __builtin_fmaf((float)is[4 * gq + 2], dx.z * dw, acc0[4 * gq + 2]);
+                                acc0[4 * gq + 3] = __builtin_fmaf((float)is[4 * gq + 3], dx.w * dw, acc0[4 * gq + 3]);
+                            }
+                        }
+                        if (two) {
+                            const v4i a = *reinterpret_cast<const v4i*>(
+                                &sA[buf][(32 + (lane & 31)) * kAPitch + bl * 32 + h * 16]);
+                            const v16i is = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop, zero, 0, 0, 0);
+#pragma unroll
+                            for (int gq = 0; gq < 4; ++gq) {
+                                const float4 dx = *reinterpret_cast<const float4*>(&sS[buf][bl][32 + 8 * gq + 4 * h]);
+                                acc1[4 * gq + 0] = __builtin_fmaf((float)is[4 * gq + 0], dx.x * dw, acc1[4 * gq + 0]);
+                                acc1[4 * gq + 1] = __builtin_fmaf((float)is[4 * gq + 1], dx.y * dw, acc1[4 * gq + 1]);
+                                acc1[4 * gq + 2] = __builtin_fmaf((float)is[4 * gq + 2], dx.z * dw, acc1[4 * gq + 2]);
+                                acc1[4 * gq + 3] = __builtin_fmaf((float)is[4 * gq + 3], dx.w * dw, acc1[4 * gq + 3]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        if (more) {
+            store_a(buf ^ 1);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                bq_cur[p] = bq_nxt[p];
+                bs_cur[p] = bs_nxt[p];
+            }
+        }
+    }
+
+    if (!wave_on) return;
+    const int j = lane & 31;
+    const int col = g.gu_f ? gu_logical_row(nt, j, g.gu_f) : nt * 32 + j;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 8 * gq + 4 * h + i;
+            if (row < nrows) g.out[(int64_t)(r0 + row) * N + col] = acc0[4 * gq + i];
+            if (row + 32 < nrows) g.out[(int64_t)(r0 + row + 32) * N + col] = acc1[4 * gq + i];
+        }
+    }
+}
+
+// -------------------------------------------------------------- combine ---
+// y[t, :] = sum_j w[t, j] * dm[pos[t*k + j], :], j ascending, fma chain from 0.
+// Also clears the membership mask for the next layer (it is dead here).
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ dm,
+                                                 const float* __restrict__ wts,
+                                                 const int32_t* __restrict__ pos, int T, int k, int d,
+                                                 float* __restrict__ y, uint32_t* __restrict__ mask,
+                                                 int64_t mask_words)
+{
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t nthreads = (int64_t)gridDim.x * 256;
+    for (int64_t i = gid; i < mask_words; i += nthreads) mask[i] = 0u;
+    const int d4 = d >> 2;
+    if (gid >= (int64_t)T * d4) return;
+    const int t = (int)(gid / d4);
+    const int c = (int)(gid - (int64_t)t * d4) * 4;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int j = 0; j < k; ++j) {
+        const int r = pos[(int64_t)t * k + j];
+        const float wt = wts[(int64_t)t * k + j];
+        const float4 v = *reinterpret_cast<const float4*>(dm + (int64_t)r * d + c);
+        acc.x = __builtin_fmaf(wt, v.x, acc.x);
+        acc.y = __builtin_fmaf(wt, v.y, acc.y);
+        acc.z = __builtin_fmaf(wt, v.z, acc.z);
+        acc.w = __builtin_fmaf(wt, v.w, acc.w);
+    }
+    *reinterpret_cast<float4*>(y + (int64_t)t * d + c) = acc;
+}
+
+__global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// ------------------------------------------------------------- launches ---
+static inline unsigned nblk(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
+{
+    const int64_t R = (int64_t)L.T * L.k;
+    hipLaunchKernelGGL(k_route, dim3(nblk(L.T, 4)), dim3(256), 0, st, L.logits, L.T, L.E, L.k,
+                       L.eidx, L.wts, L.mask, L.W);
+    const int64_t xblocks = (int64_t)L.T * (L.d / 32);
+    hipLaunchKernelGGL(k_quant_q8, dim3(nblk(xblocks * 8, 256)), dim3(256), 0, st, L.x, xblocks,
+                       L.xq, L.dx);
+    hipLaunchKernelGGL(k_group_prefix, dim3(L.E), dim3(256), 0, st, L.mask, L.W, L.wprefix,
+                       L.counts);
+    hipLaunchKernelGGL(k_group_bounds, dim3(1), dim3(1024), 0, st, L.counts, L.E, L.bounds, L.tiles,
+                       L.ntiles);
+    hipLaunchKernelGGL(k_scatter, dim3(nblk(R, 256)), dim3(256), 0, st, L.eidx, R, L.k, L.mask,
+                       L.wprefix, L.bounds, L.W, L.rows, L.pos, L.rtok);
+    const int max_tiles_now = (int)((R + kBM - 1) / kBM) + (L.E < R ? L.E : (int)R);
+
+    GemmArgs gu;
+    gu.A = L.xq;
+    gu.A_scale = L.dx;
+    gu.row_src = L.rtok;
+    gu.blob = L.blob;
+    gu.expert_stride = L.expert_stride;
+    gu.q_off = L.gu_q_off;
+    gu.s_off = L.gu_s_off;
+    gu.tiles = L.tiles;
+    gu.ntiles = L.ntiles;
+    gu.out = L.gu;
+    gu.N = 2 * L.f;
+    gu.K = L.d;
+    gu.gu_f = L.f;
+    hipLaunchKernelGGL(k_grouped_gemm, dim3(nblk(gu.N / 32, 4), max_tiles_now), dim3(256), 0, st, gu);
+
+    const int64_t hblocks = R * (L.f / 32);
+    hipLaunchKernelGGL(k_swiglu_q8, dim3(nblk(hblocks * 8, 256)), dim3(256), 0, st, L.gu, R, L.f,
+                       L.hq, L.dh, L.h_out);
+
+    GemmArgs dn = gu;
+    dn.A = L.hq;
+    dn.A_scale = L.dh;
+    dn.row_src = nullptr;
+    dn.q_off = L.d_q_off;
+    dn.s_off = L.d_s_off;
+    dn.out = L.dm;
+    dn.N = L.d;
+    dn.K = L.f;
+    dn.gu_f = 0;
+    hipLaunchKernelGGL(k_grouped_gemm, dim3(nblk(dn.N / 32, 4), max_tiles_now), dim3(256), 0, st, dn);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const LayerLaunch& L, hipStream_t st)
+{
+    const int64_t work = (int64_t)L.T * (L.d / 4);
+    const int64_t mw = (int64_t)L.E * L.W;
+    hipLaunchKernelGGL(k_combine, dim3(nblk(work > mw ? work : mw, 256)), dim3(256), 0, st, L.dm,
+                       L.wts, L.pos, L.T, L.k, L.d, L.y, L.mask, mw);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st)
+{
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_u32, dim3(nblk(n, 256)), dim3(256), 0, st, p, n, v);
+    return hipGetLastError();
+}
+
+}  // namespace moe

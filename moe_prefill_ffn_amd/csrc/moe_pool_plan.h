@@ -1,0 +1,26 @@
+// Slot-pool planner (pure; no device calls).
+#pragma once
+
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWarnSlotOverBudget = 1;
+constexpr int kWarnPoolDegraded = 2;
+constexpr int kWarnDepthReduced = 4;
+
+struct PoolShape {
+    int slots = 0;       // total slots = residents + (residents < L ? 1 + depth : 0)
+    int depth = 0;       // prefetch lookahead
+    int residents = 0;   // resident leading layers
+};
+
+// First plan for L layers (L >= 1).
+PoolShape plan_initial(int L, uint64_t slot_bytes, int depth_req, int residents_req,
+                       int64_t budget, int requested_slots, int* warnings);
+
+// The next smaller pool after an allocation of cur.slots slots failed
+// (cur.slots >= 2): one slot fewer, prefetch window kept before residents.
+PoolShape plan_degrade(const PoolShape& cur, int L, int depth_req, int residents_req, int* warnings);
+
+}  // namespace moe

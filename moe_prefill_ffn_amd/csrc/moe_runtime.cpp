@@ -1,0 +1,697 @@
+// Host runtime behind the C ABI (include/moe_prefill.h): handle + workspace,
+// layer launch, fixed-slot pool with a lookahead prefetch queue on its own
+// HIP stream, event fencing, stats and errors.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <chrono>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/moe_prefill.h"
+#include "moe_kernels.h"
+#include "moe_layout.h"
+#include "moe_pool_plan.h"
+
+namespace moe {
+bool pack_expert(int d, int f, const int8_t* wgu_q, const uint16_t* wgu_s, const int8_t* wd_q,
+                 const uint16_t* wd_s, uint8_t* dst);
+}
+
+using namespace moe;
+
+struct moe_prefill {
+    int dev = 0;
+    int d = 0, f = 0, E = 0, k = 0, Tmax = 0;
+    WsLayout L{};
+    BlobLayout B{};
+    uint8_t* ws = nullptr;
+    bool ws_owned = false;
+    hipStream_t copy = nullptr;
+    std::string err;
+    bool mask_dirty = false;
+
+    // stream pool
+    bool pool_on = false;
+    int nl = 0;
+    std::vector<const void*> blobs;
+    uint64_t layer_bytes = 0, slot_bytes = 0;
+    PoolShape shape;
+    int warnings = 0;
+    uint8_t* pool = nullptr;
+    std::vector<int> slot_layer, layer_slot;
+    std::vector<hipEvent_t> ev_ready, ev_free;
+    std::vector<char> ready_set, free_set, from_prefetch;
+    int active = -1;
+    uint64_t prefetch_counter = 0;
+    uint64_t fail_at = 0;   // test hook: this prefetch enqueue (1-based) is treated as failed
+
+    moe_stats_t stats{};
+};
+
+static thread_local std::string g_err;
+
+static int fail(moe_prefill_t* h, int code, const std::string& msg)
+{
+    if (h)
+        h->err = msg;
+    else
+        g_err = msg;
+    return code;
+}
+
+static int hip_fail(moe_prefill_t* h, hipError_t e, const char* what)
+{
+    return fail(h, MOE_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+namespace {
+
+struct DevGuard {
+    int prev = -1;
+    explicit DevGuard(int d)
+    {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        (void)hipSetDevice(d);
+    }
+    ~DevGuard()
+    {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+// Versioned struct in: a smaller struct_size leaves trailing fields at 0; a
+// larger one is accepted only if every unknown byte is zero.
+template <class S>
+bool read_struct(const void* src, S* dst, std::string* why)
+{
+    memset(dst, 0, sizeof(S));
+    if (!src) {
+        *why = "null struct pointer";
+        return false;
+    }
+    uint32_t sz;
+    memcpy(&sz, src, 4);
+    if (sz < 8) {
+        *why = "struct_size too small";
+        return false;
+    }
+    if (sz <= sizeof(S)) {
+        memcpy(dst, src, sz);
+    } else {
+        memcpy(dst, src, sizeof(S));
+        const uint8_t* b = static_cast<const uint8_t*>(src);
+        for (uint32_t i = sizeof(S); i < sz; ++i)
+            if (b[i]) {
+                *why = "struct_size larger than this library knows, with nonzero unknown fields";
+                return false;
+            }
+    }
+    dst->struct_size = sizeof(S);
+    return true;
+}
+
+template <class S>
+void write_struct(void* dst, const S& src)
+{
+    uint32_t sz;
+    memcpy(&sz, dst, 4);
+    S tmp = src;
+    const uint32_t n = sz < sizeof(S) ? sz : (uint32_t)sizeof(S);
+    memcpy(dst, &tmp, n);
+    memcpy(dst, &sz, 4);   // keep the caller's struct_size
+}
+
+int64_t wait_budget_ms()
+{
+    const char* s = getenv("MOE_WAIT_MS");
+    return s ? atoll(s) : 120000;
+}
+
+// Bounded host waits (a wait that expires returns MOE_ETIMEOUT).
+int wait_stream(moe_prefill_t* h, hipStream_t st)
+{
+    const auto t0 = std::chrono::steady_clock::now();
+    const int64_t lim = wait_budget_ms();
+    for (;;) {
+        const hipError_t e = hipStreamQuery(st);
+        if (e == hipSuccess) return MOE_OK;
+        if (e != hipErrorNotReady) return hip_fail(h, e, "hipStreamQuery");
+        const auto ms = std::chrono::duration_cast<std::chrono::milliseconds>(
+                            std::chrono::steady_clock::now() - t0).count();
+        if (lim > 0 && ms > lim) return fail(h, MOE_ETIMEOUT, "copy stream wait timed out");
+        std::this_thread::sleep_for(std::chrono::microseconds(50));
+    }
+}
+
+int wait_event(moe_prefill_t* h, hipEvent_t ev)
+{
+    const auto t0 = std::chrono::steady_clock::now();
+    const int64_t lim = wait_budget_ms();
+    for (;;) {
+        const hipError_t e = hipEventQuery(ev);
+        if (e == hipSuccess) return MOE_OK;
+        if (e != hipErrorNotReady) return hip_fail(h, e, "hipEventQuery");
+        const auto ms = std::chrono::duration_cast<std::chrono::milliseconds>(
+                            std::chrono::steady_clock::now() - t0).count();
+        if (lim > 0 && ms > lim) return fail(h, MOE_ETIMEOUT, "event wait timed out");
+        std::this_thread::sleep_for(std::chrono::microseconds(50));
+    }
+}
+
+bool dims_ok(const moe_prefill_params_t& p, std::string* why)
+{
+    auto bad = [&](const char* m) {
+        *why = m;
+        return false;
+    };
+    if (p.d_model < 64 || p.d_model > 16384 || p.d_model % 64) return bad("d_model must be a multiple of 64 in [64, 16384]");
+    if (p.d_ff < 64 || p.d_ff > 16384 || p.d_ff % 64) return bad("d_ff must be a multiple of 64 in [64, 16384]");
+    if (p.n_experts < 1 || p.n_experts > 1024) return bad("n_experts must be in [1, 1024]");
+    if (p.top_k < 1 || p.top_k > p.n_experts || p.top_k > 64) return bad("top_k must be in [1, min(n_experts, 64)]");
+    if (p.max_tokens < 1 || (int64_t)p.max_tokens * p.top_k > (1 << 21)) return bad("max_tokens must be >= 1 and max_tokens*top_k <= 2^21");
+    return true;
+}
+
+// --------------------------------------------------------------- pool ops ---
+
+// Layers of the prefetch window after `cur`: the next `depth` streamed layers
+// in pass order (wrapping to the next pass), never `cur` itself.
+std::vector<int> window_after(const moe_prefill_t* h, int cur)
+{
+    std::vector<int> w;
+    const int res = h->shape.residents;
+    if (res >= h->nl) return w;
+    for (int i = 1; i < h->nl && (int)w.size() < h->shape.depth; ++i) {
+        const int y = (cur + i) % h->nl;
+        if (y >= res && y != cur) w.push_back(y);
+    }
+    return w;
+}
+
+// Streaming slot to (re)fill: not `exclude`, not holding `cur` or a layer of
+// cur's window; an empty slot first, else the one whose layer comes last.
+int pick_victim(const moe_prefill_t* h, int cur, int exclude)
+{
+    const std::vector<int> win = window_after(h, cur);
+    int best = -1;
+    long best_score = -1;
+    for (int s = h->shape.residents; s < h->shape.slots; ++s) {
+        if (s == exclude) continue;
+        const int lay = h->slot_layer[s];
+        bool keep = lay >= 0 && lay == cur;
+        for (int y : win) keep = keep || lay == y;
+        if (keep) continue;
+        const long score = lay < 0 ? (1L << 40) : (long)((lay - cur + h->nl) % h->nl);
+        if (score > best_score) {
+            best_score = score;
+            best = s;
+        }
+    }
+    return best;
+}
+
+hipError_t enqueue_copy(moe_prefill_t* h, int s, int layer)
+{
+    const int old = h->slot_layer[s];
+    if (old >= 0) h->layer_slot[old] = -1;
+    h->slot_layer[s] = -1;
+    h->from_prefetch[s] = 0;
+    hipError_t e = hipSuccess;
+    if (h->free_set[s]) e = hipStreamWaitEvent(h->copy, h->ev_free[s], 0);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(h->pool + (uint64_t)s * h->slot_bytes, h->blobs[layer], h->layer_bytes,
+                           hipMemcpyHostToDevice, h->copy);
+    if (e == hipSuccess) e = hipEventRecord(h->ev_ready[s], h->copy);
+    if (e != hipSuccess) return e;
+    h->ready_set[s] = 1;
+    h->slot_layer[s] = layer;
+    h->layer_slot[layer] = s;
+    h->stats.bytes_h2d += h->layer_bytes;
+    return hipSuccess;
+}
+
+void pool_release(moe_prefill_t* h)
+{
+    if (!h->pool_on && !h->pool) return;
+    (void)wait_stream(h, h->copy);
+    for (size_t s = 0; s < h->ev_free.size(); ++s)
+        if (h->free_set[s]) (void)wait_event(h, h->ev_free[s]);
+    for (hipEvent_t e : h->ev_ready) (void)hipEventDestroy(e);
+    for (hipEvent_t e : h->ev_free) (void)hipEventDestroy(e);
+    if (h->pool) (void)hipFree(h->pool);
+    h->pool = nullptr;
+    h->pool_on = false;
+    h->nl = 0;
+    h->blobs.clear();
+    h->slot_layer.clear();
+    h->layer_slot.clear();
+    h->ev_ready.clear();
+    h->ev_free.clear();
+    h->ready_set.clear();
+    h->free_set.clear();
+    h->from_prefetch.clear();
+    h->active = -1;
+    h->shape = PoolShape();
+    h->warnings = 0;
+}
+
+}  // namespace
+
+// ======================================================================= ABI
+
+extern "C" {
+
+const char* moe_prefill_last_error(const moe_prefill_t* h)
+{
+    return h ? h->err.c_str() : g_err.c_str();
+}
+
+uint64_t moe_prefill_expert_bytes(int32_t d_model, int32_t d_ff)
+{
+    if (d_model < 64 || d_model % 64 || d_ff < 64 || d_ff % 64) return 0;
+    return blob_layout(d_model, d_ff).expert_bytes;
+}
+
+uint64_t moe_prefill_layer_bytes(int32_t d_model, int32_t d_ff, int32_t n_experts)
+{
+    if (n_experts < 1) return 0;
+    return moe_prefill_expert_bytes(d_model, d_ff) * (uint64_t)n_experts;
+}
+
+int moe_prefill_pack_expert(int32_t d_model, int32_t d_ff, const int8_t* wgu_q, const uint16_t* wgu_s,
+                            const int8_t* wd_q, const uint16_t* wd_s, void* dst)
+{
+    if (d_model < 64 || d_model % 64 || d_ff < 64 || d_ff % 64 || d_model > 16384 || d_ff > 16384)
+        return fail(nullptr, MOE_EINVAL, "pack: d_model and d_ff must be multiples of 64 in [64, 16384]");
+    if (!wgu_q || !wgu_s || !wd_q || !wd_s || !dst) return fail(nullptr, MOE_EINVAL, "pack: null pointer");
+    if (!pack_expert(d_model, d_ff, wgu_q, wgu_s, wd_q, wd_s, static_cast<uint8_t*>(dst)))
+        return fail(nullptr, MOE_EINVAL, "pack: weight outside [-8, 7]");
+    return MOE_OK;
+}
+
+int moe_prefill_workspace_size(const moe_prefill_params_t* pin, uint64_t* bytes)
+{
+    moe_prefill_params_t p;
+    std::string why;
+    if (!bytes) return fail(nullptr, MOE_EINVAL, "null bytes pointer");
+    if (!read_struct(pin, &p, &why)) return fail(nullptr, MOE_EINVAL, why);
+    if (!dims_ok(p, &why)) return fail(nullptr, MOE_EINVAL, why);
+    *bytes = ws_layout(p.d_model, p.d_ff, p.n_experts, p.top_k, p.max_tokens).total;
+    return MOE_OK;
+}
+
+int moe_prefill_create(const moe_prefill_params_t* pin, moe_prefill_t** out)
+{
+    if (!out) return fail(nullptr, MOE_EINVAL, "null out pointer");
+    *out = nullptr;
+    moe_prefill_params_t p;
+    std::string why;
+    if (!read_struct(pin, &p, &why)) return fail(nullptr, MOE_EINVAL, why);
+    if (!dims_ok(p, &why)) return fail(nullptr, MOE_EINVAL, why);
+
+    int ndev = 0;
+    hipError_t e = hipGetDeviceCount(&ndev);
+    if (e != hipSuccess || ndev < 1) return fail(nullptr, MOE_EUNSUPPORTED, "no HIP device");
+    if (p.device < 0 || p.device >= ndev) return fail(nullptr, MOE_EINVAL, "device ordinal out of range");
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, p.device);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "hipGetDeviceProperties");
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(nullptr, MOE_EUNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", not gfx950");
+
+    DevGuard guard(p.device);
+    moe_prefill_t* h = new moe_prefill_t();
+    h->dev = p.device;
+    h->d = p.d_model;
+    h->f = p.d_ff;
+    h->E = p.n_experts;
+    h->k = p.top_k;
+    h->Tmax = p.max_tokens;
+    h->L = ws_layout(h->d, h->f, h->E, h->k, h->Tmax);
+    h->B = blob_layout(h->d, h->f);
+    h->stats.struct_size = sizeof(moe_stats_t);
+
+    if (p.workspace) {
+        if (p.workspace_bytes < h->L.total) {
+            delete h;
+            return fail(nullptr, MOE_EINVAL, "lent workspace smaller than moe_prefill_workspace_size()");
+        }
+        if (reinterpret_cast<uintptr_t>(p.workspace) % 256) {
+            delete h;
+            return fail(nullptr, MOE_EINVAL, "lent workspace must be 256-byte aligned");
+        }
+        h->ws = static_cast<uint8_t*>(p.workspace);
+    } else {
+        e = hipMalloc(reinterpret_cast<void**>(&h->ws), h->L.total);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            delete h;
+            return fail(nullptr, MOE_ENOMEM, "workspace allocation failed");
+        }
+        h->ws_owned = true;
+    }
+    e = hipStreamCreateWithFlags(&h->copy, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipMemset(h->ws + h->L.mask, 0, (size_t)h->E * h->L.W * 4);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        const int rc = hip_fail(nullptr, e, "create");
+        if (h->copy) (void)hipStreamDestroy(h->copy);
+        if (h->ws_owned) (void)hipFree(h->ws);
+        delete h;
+        return rc;
+    }
+    *out = h;
+    g_err.clear();
+    return MOE_OK;
+}
+
+void moe_prefill_destroy(moe_prefill_t* h)
+{
+    if (!h) return;
+    {
+        DevGuard guard(h->dev);
+        pool_release(h);
+        if (h->copy) (void)hipStreamDestroy(h->copy);
+        if (h->ws_owned && h->ws) (void)hipFree(h->ws);
+    }
+    delete h;
+}
+
+int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* stream)
+{
+    if (!h) return fail(nullptr, MOE_EINVAL, "null handle");
+    moe_layer_io_t io;
+    std::string why;
+    if (!read_struct(io_in, &io, &why)) return fail(h, MOE_EINVAL, why);
+    const int T = io.n_tokens;
+    if (T < 0 || T > h->Tmax) return fail(h, MOE_EINVAL, "n_tokens out of [0, max_tokens]");
+    if (T == 0) return MOE_OK;
+    if (!io.x || !io.logits || !io.y) return fail(h, MOE_EINVAL, "x, logits and y are required");
+    if ((reinterpret_cast<uintptr_t>(io.x) | reinterpret_cast<uintptr_t>(io.y) |
+         reinterpret_cast<uintptr_t>(io.h)) % 16)
+        return fail(h, MOE_EINVAL, "x, y and h must be 16-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    DevGuard guard(h->dev);
+
+    const uint8_t* blob = nullptr;
+    int slot = -1;
+    hipError_t e = hipSuccess;
+    if (io.layer < 0) {
+        if (!io.weights_dev) return fail(h, MOE_EINVAL, "layer == -1 needs weights_dev");
+        blob = static_cast<const uint8_t*>(io.weights_dev);
+    } else {
+        if (!h->pool_on) return fail(h, MOE_ESTATE, "layer >= 0 but no stream pool is configured");
+        if (io.layer >= h->nl) return fail(h, MOE_ESTATE, "layer index beyond the configured stack");
+        slot = h->layer_slot[io.layer];
+        if (slot >= 0) {
+            if (slot >= h->shape.residents && h->ready_set[slot])
+                e = hipStreamWaitEvent(st, h->ev_ready[slot], 0);
+            if (h->from_prefetch[slot]) {
+                h->stats.prefetch_activated++;
+                h->from_prefetch[slot] = 0;
+            }
+        } else {
+            // load-then-compute: a stream-ordered copy into a free slot first
+            slot = pick_victim(h, io.layer, -1);
+            if (slot < 0) return fail(h, MOE_ESTATE, "no pool slot available");
+            e = enqueue_copy(h, slot, io.layer);
+            if (e == hipSuccess) e = hipStreamWaitEvent(st, h->ev_ready[slot], 0);
+            h->stats.sync_loads++;
+        }
+        if (e != hipSuccess) return hip_fail(h, e, "pool acquire");
+        blob = h->pool + (uint64_t)slot * h->slot_bytes;
+    }
+
+    if (h->mask_dirty) {
+        e = launch_fill_u32(reinterpret_cast<uint32_t*>(h->ws + h->L.mask), (int64_t)h->E * h->L.W, 0u, st);
+        if (e != hipSuccess) return hip_fail(h, e, "mask clear");
+        h->mask_dirty = false;
+    }
+
+    uint8_t* w = h->ws;
+    LayerLaunch LL;
+    LL.T = T;
+    LL.d = h->d;
+    LL.f = h->f;
+    LL.E = h->E;
+    LL.k = h->k;
+    LL.W = h->L.W;
+    LL.x = io.x;
+    LL.logits = io.logits;
+    LL.y = io.y;
+    LL.blob = blob;
+    LL.expert_stride = h->B.expert_bytes;
+    LL.gu_q_off = h->B.gu_q;
+    LL.gu_s_off = h->B.gu_s;
+    LL.d_q_off = h->B.d_q;
+    LL.d_s_off = h->B.d_s;
+    LL.eidx = reinterpret_cast<int32_t*>(w + h->L.eidx);
+    LL.wts = reinterpret_cast<float*>(w + h->L.wts);
+    LL.mask = reinterpret_cast<uint32_t*>(w + h->L.mask);
+    LL.wprefix = reinterpret_cast<int32_t*>(w + h->L.wprefix);
+    LL.counts = reinterpret_cast<int32_t*>(w + h->L.counts);
+    LL.bounds = reinterpret_cast<int32_t*>(w + h->L.bounds);
+    LL.tiles = reinterpret_cast<int32_t*>(w + h->L.tiles);
+    LL.ntiles = reinterpret_cast<int32_t*>(w + h->L.ntiles);
+    LL.rows = reinterpret_cast<int32_t*>(w + h->L.rows);
+    LL.pos = reinterpret_cast<int32_t*>(w + h->L.pos);
+    LL.rtok = reinterpret_cast<int32_t*>(w + h->L.rtok);
+    LL.xq = reinterpret_cast<int8_t*>(w + h->L.xq);
+    LL.dx = reinterpret_cast<float*>(w + h->L.dx);
+    LL.gu = reinterpret_cast<float*>(w + h->L.gu);
+    LL.hq = reinterpret_cast<int8_t*>(w + h->L.hq);
+    LL.dh = reinterpret_cast<float*>(w + h->L.dh);
+    LL.dm = reinterpret_cast<float*>(w + h->L.dm);
+    LL.h_out = io.h;
+
+    e = launch_layer(LL, st);
+    if (e != hipSuccess) {
+        h->mask_dirty = true;
+        return hip_fail(h, e, "layer launch");
+    }
+    if (slot >= 0) {
+        e = hipEventRecord(h->ev_free[slot], st);   // the down GEMM was the last reader
+        if (e != hipSuccess) {
+            h->mask_dirty = true;
+            return hip_fail(h, e, "hipEventRecord");
+        }
+        h->free_set[slot] = 1;
+        h->active = slot;
+    }
+    e = launch_combine(LL, st);
+    if (e != hipSuccess) {
+        h->mask_dirty = true;
+        return hip_fail(h, e, "combine launch");
+    }
+
+    // optional exports of the intermediate buffers
+    const uint64_t R = (uint64_t)T * h->k;
+    struct Ex {
+        void* dst;
+        uint64_t off, bytes;
+    } ex[] = {
+        {io.eidx, h->L.eidx, R * 4},
+        {io.weights, h->L.wts, R * 4},
+        {io.counts, h->L.counts, (uint64_t)h->E * 4},
+        {io.bounds, h->L.bounds, (uint64_t)(h->E + 1) * 4},
+        {io.rows, h->L.rows, R * 4},
+        {io.pos, h->L.pos, R * 4},
+        {io.xq, h->L.xq, (uint64_t)T * h->d},
+        {io.dx, h->L.dx, (uint64_t)T * (h->d / 32) * 4},
+        {io.gu, h->L.gu, R * 2 * h->f * 4},
+        {io.hq, h->L.hq, R * h->f},
+        {io.dh, h->L.dh, R * (h->f / 32) * 4},
+        {io.dm, h->L.dm, R * h->d * 4},
+    };
+    for (const Ex& x : ex) {
+        if (!x.dst) continue;
+        e = hipMemcpyAsync(x.dst, h->ws + x.off, x.bytes, hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return hip_fail(h, e, "export copy");
+    }
+    h->stats.layers_run++;
+
+    // lookahead: queue the next streamed layers behind this one
+    if (io.layer >= 0) {
+        for (int y : window_after(h, io.layer)) {
+            if (h->layer_slot[y] >= 0) continue;
+            const int v = pick_victim(h, io.layer, h->active);
+            if (v < 0) break;
+            h->prefetch_counter++;
+            if (h->fail_at && h->prefetch_counter == h->fail_at) {
+                h->stats.prefetch_failed++;   // forced failure: this layer will load synchronously
+                continue;
+            }
+            e = enqueue_copy(h, v, y);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                h->stats.prefetch_failed++;
+                continue;
+            }
+            h->from_prefetch[v] = 1;
+            h->stats.prefetch_queued++;
+        }
+    }
+    h->err.clear();
+    return MOE_OK;
+}
+
+int moe_prefill_plan_pool(moe_pool_plan_t* inout)
+{
+    moe_pool_plan_t p;
+    std::string why;
+    if (!read_struct(inout, &p, &why)) return fail(nullptr, MOE_EINVAL, why);
+    if (p.n_layers < 0 || p.prefetch_depth < 0 || p.resident_layers < -1)
+        return fail(nullptr, MOE_EINVAL, "plan: bad request");
+    p.slots = p.depth = p.residents = p.warnings = 0;
+    if (p.n_layers == 0) {
+        write_struct(inout, p);
+        return MOE_OK;
+    }
+    if (p.slot_bytes == 0) return fail(nullptr, MOE_EINVAL, "plan: slot_bytes == 0");
+    int warn = 0;
+    PoolShape s = plan_initial(p.n_layers, p.slot_bytes, p.prefetch_depth, p.resident_layers,
+                               p.max_vram_bytes, p.requested_slots, &warn);
+    for (;;) {
+        const bool fits = p.max_alloc_slots == 0 || (p.max_alloc_slots > 0 && s.slots <= p.max_alloc_slots);
+        if (fits) break;
+        if (s.slots <= 1) {
+            p.warnings = warn;
+            write_struct(inout, p);
+            return fail(nullptr, MOE_ENOMEM, "plan: one slot does not fit");
+        }
+        s = plan_degrade(s, p.n_layers, p.prefetch_depth, p.resident_layers, &warn);
+    }
+    p.slots = s.slots;
+    p.depth = s.depth;
+    p.residents = s.residents;
+    p.warnings = warn;
+    write_struct(inout, p);
+    return MOE_OK;
+}
+
+int stream_pool_configure(moe_prefill_t* h, stream_pool_params_t* inout)
+{
+    if (!h) return fail(nullptr, MOE_EINVAL, "null handle");
+    stream_pool_params_t p;
+    std::string why;
+    if (!read_struct(inout, &p, &why)) return fail(h, MOE_EINVAL, why);
+    DevGuard guard(h->dev);
+
+    // a new plan first releases stale prefetches and residents
+    int rc = wait_stream(h, h->copy);
+    if (rc != MOE_OK) return rc;
+    pool_release(h);
+    p.eff_slots = p.eff_depth = p.eff_residents = p.warnings = 0;
+    h->stats.eff_slots = h->stats.eff_depth = h->stats.eff_residents = h->stats.warnings = 0;
+    if (p.n_layers == 0) {
+        write_struct(inout, p);
+        return MOE_OK;
+    }
+    if (p.n_layers < 0 || !p.host_blobs) return fail(h, MOE_EINVAL, "pool: need n_layers > 0 and host_blobs");
+    if (p.prefetch_depth < 0 || p.resident_layers < -1) return fail(h, MOE_EINVAL, "pool: bad depth or resident count");
+    const uint64_t want = blob_layout(h->d, h->f).expert_bytes * (uint64_t)h->E;
+    if (p.layer_bytes != want) return fail(h, MOE_EINVAL, "pool: layer_bytes != moe_prefill_layer_bytes()");
+    for (int i = 0; i < p.n_layers; ++i)
+        if (!p.host_blobs[i]) return fail(h, MOE_EINVAL, "pool: null host blob");
+
+    const uint64_t slot_bytes = align_up(p.layer_bytes, 1 << 16);
+    int warn = 0;
+    PoolShape s = plan_initial(p.n_layers, slot_bytes, p.prefetch_depth, p.resident_layers,
+                               p.max_vram_bytes, p.requested_slots, &warn);
+    const char* cap_env = getenv("MOE_TEST_POOL_MAX_SLOTS");
+    const int cap = cap_env ? atoi(cap_env) : 0;
+    const bool fail_all = getenv("MOE_TEST_POOL_FAIL_ALL") && atoi(getenv("MOE_TEST_POOL_FAIL_ALL"));
+    uint8_t* pool = nullptr;
+    for (;;) {
+        bool ok = !fail_all && !(cap > 0 && s.slots > cap);
+        if (ok) {
+            const hipError_t e = hipMalloc(reinterpret_cast<void**>(&pool), (size_t)s.slots * slot_bytes);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                pool = nullptr;
+                ok = false;
+            }
+        }
+        if (ok) break;
+        if (s.slots <= 1) {
+            p.warnings = warn;
+            write_struct(inout, p);
+            return fail(h, MOE_ENOMEM, "pool: the mandatory one-slot pool could not be allocated");
+        }
+        s = plan_degrade(s, p.n_layers, p.prefetch_depth, p.resident_layers, &warn);
+    }
+
+    h->pool = pool;
+    h->pool_on = true;
+    h->nl = p.n_layers;
+    h->blobs.assign(p.host_blobs, p.host_blobs + p.n_layers);
+    h->layer_bytes = p.layer_bytes;
+    h->slot_bytes = slot_bytes;
+    h->shape = s;
+    h->warnings = warn;
+    h->slot_layer.assign(s.slots, -1);
+    h->layer_slot.assign(p.n_layers, -1);
+    h->ev_ready.assign(s.slots, nullptr);
+    h->ev_free.assign(s.slots, nullptr);
+    h->ready_set.assign(s.slots, 0);
+    h->free_set.assign(s.slots, 0);
+    h->from_prefetch.assign(s.slots, 0);
+    h->active = -1;
+    h->prefetch_counter = 0;
+    const char* fa = getenv("MOE_TEST_PREFETCH_FAIL");
+    h->fail_at = fa ? (uint64_t)atoll(fa) : 0;
+    for (int i = 0; i < s.slots; ++i) {
+        hipError_t e = hipEventCreateWithFlags(&h->ev_ready[i], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_free[i], hipEventDisableTiming);
+        if (e != hipSuccess) {
+            const int r = hip_fail(h, e, "pool events");
+            pool_release(h);
+            return r;
+        }
+    }
+    // resident leading layers are uploaded now
+    for (int i = 0; i < s.residents; ++i) {
+        const hipError_t e = hipMemcpyAsync(h->pool + (uint64_t)i * slot_bytes, h->blobs[i], h->layer_bytes,
+                                            hipMemcpyHostToDevice, h->copy);
+        if (e != hipSuccess) {
+            const int r = hip_fail(h, e, "resident upload");
+            pool_release(h);
+            return r;
+        }
+        h->slot_layer[i] = i;
+        h->layer_slot[i] = i;
+        h->stats.bytes_h2d += h->layer_bytes;
+    }
+    rc = wait_stream(h, h->copy);
+    if (rc != MOE_OK) {
+        pool_release(h);
+        return rc;
+    }
+    p.eff_slots = s.slots;
+    p.eff_depth = s.depth;
+    p.eff_residents = s.residents;
+    p.warnings = warn;
+    h->stats.eff_slots = s.slots;
+    h->stats.eff_depth = s.depth;
+    h->stats.eff_residents = s.residents;
+    h->stats.warnings = warn;
+    write_struct(inout, p);
+    h->err.clear();
+    return MOE_OK;
+}
+
+int moe_prefill_get_stats(const moe_prefill_t* h, moe_stats_t* inout)
+{
+    if (!h) return fail(nullptr, MOE_EINVAL, "null handle");
+    moe_stats_t tmp;
+    std::string why;
+    if (!read_struct(inout, &tmp, &why)) return fail(nullptr, MOE_EINVAL, why);
+    write_struct(inout, h->stats);
+    return MOE_OK;
+}
+
+}  // extern "C"

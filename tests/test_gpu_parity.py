@@ -1,0 +1,178 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, stage by
+stage, on seeded synthetic layers -- the tiny and real-shape resident layers in
+full, edge cases (ragged T, single token, one expert, E not a multiple of 64,
+partial K stages, empty experts, ties, zero input), and the large skewed /
+biased shapes on sampled rows and tokens in the bench's launch configuration.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_prefill_ffn_amd as mp
+import oracle
+import workload as wl
+from gpu_helpers import (ExpertCache, assert_close, assert_equal, check_full_parity,
+                         check_sampled_parity, host_blob, make_handle, run_layer_gpu, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_case(w, layer=0, x=None, lg=None, override=None, max_tokens=None):
+    say(f"[case] {w.name} layer {layer}")
+    x = wl.layer_activations(w, layer) if x is None else x
+    lg = wl.layer_logits(w, layer) if lg is None else lg
+    ex = ExpertCache(w, layer, override=override)
+    blob = host_blob(w, ex).cuda()
+    h = make_handle(w, max_tokens)
+    g = run_layer_gpu(h, w, x, lg, blob)
+    ref = oracle.layer(x, lg, w.k, ex, w.f)
+    h.close()
+    return g, ref
+
+
+def test_tiny_layer_all_stages():
+    w = wl.WORKLOADS["tiny"]
+    g, ref = _full_case(w)
+    check_full_parity(w, g, ref)
+
+
+def test_resident_real_shape_all_stages():
+    w = wl.WORKLOADS["resident"]
+    g, ref = _full_case(w)
+    check_full_parity(w, g, ref)
+
+
+@pytest.mark.parametrize("T,d,f,E,k,bias", [
+    (1, 256, 512, 8, 2, None),          # a single token
+    (97, 128, 192, 16, 3, None),        # ragged T, f/64 = 3 (partial K stage), odd k
+    (200, 64, 64, 130, 7, None),        # E not a multiple of 64, minimal d and f
+    (65, 128, 128, 1, 1, None),         # one expert: 65 rows = a full tile + 1 row
+    (64, 128, 128, 1, 1, None),         # exactly one full 64-row tile
+    (300, 256, 256, 64, 4, ("zipf", 1.1)),   # many empty experts
+    (129, 192, 320, 5, 5, None),        # k = E: every expert gets every token
+])
+def test_edge_shapes(T, d, f, E, k, bias):
+    w = wl.small_workload(T, d, f, E, k, seed_base=77 + T + E, bias=bias)
+    g, ref = _full_case(w)
+    check_full_parity(w, g, ref)
+    if bias:
+        assert (ref["counts"] == 0).sum() > 0     # the case really has empty experts
+
+
+def test_tied_logits_pick_lowest_experts():
+    w = wl.small_workload(40, 128, 128, 12, 4, seed_base=5)
+    lg = np.zeros((w.T, w.E), np.float32)
+    lg[::2, 7] = 1.0                       # even tokens: expert 7 first, then 0, 1, 2
+    lg[1::3, 3] = -0.0                     # -0 ties with +0
+    g, ref = _full_case(w, lg=lg)
+    check_full_parity(w, g, ref)
+    assert np.array_equal(g["eidx"][1], [0, 1, 2, 3])
+    assert np.array_equal(g["eidx"][0], [7, 0, 1, 2])
+
+
+def test_zero_activations_give_zero_output():
+    w = wl.small_workload(50, 128, 192, 8, 2, seed_base=9)
+    x = np.zeros((w.T, w.d), np.float32)
+    g, ref = _full_case(w, x=x)
+    check_full_parity(w, g, ref)
+    assert np.all(g["y"] == 0) and np.all(g["xq"] == 0)
+
+
+def test_tiny_and_huge_magnitudes():
+    w = wl.small_workload(64, 128, 128, 8, 2, seed_base=11)
+    x = wl.layer_activations(w, 0) * np.float32(1e-30)
+    x[3] *= np.float32(1e-8)                # denormal scales
+    x[5] = wl.layer_activations(w, 0)[5] * np.float32(1e10)
+    g, ref = _full_case(w, x=x)
+    check_full_parity(w, g, ref)
+
+
+def test_fewer_tokens_than_max_and_repeat_runs_are_identical():
+    w = wl.WORKLOADS["tiny"]
+    x = wl.layer_activations(w, 0)
+    lg = wl.layer_logits(w, 0)
+    ex = ExpertCache(w, 0)
+    blob = host_blob(w, ex).cuda()
+    h = make_handle(w, max_tokens=4 * w.T)
+    g1 = run_layer_gpu(h, w, x, lg, blob)
+    g2 = run_layer_gpu(h, w, x[:17], lg[:17], blob)
+    g3 = run_layer_gpu(h, w, x, lg, blob)
+    ref = oracle.layer(x, lg, w.k, ex, w.f)
+    ref17 = oracle.layer(x[:17], lg[:17], w.k, ex, w.f)
+    check_full_parity(w, g1, ref)
+    check_full_parity(w, g2, ref17)
+    for k in g1:
+        assert_equal(k, g3[k], g1[k])
+    # T = 0 is a no-op
+    y0 = torch.zeros(0, w.d, device="cuda")
+    mp.moe_prefill_run_layer(h, torch.zeros(0, w.d, device="cuda"), torch.zeros(0, w.E, device="cuda"),
+                             y0, weights=blob)
+    h.close()
+
+
+def test_bad_arguments_fail_clearly():
+    w = wl.WORKLOADS["tiny"]
+    h = make_handle(w)
+    x = torch.zeros(w.T + 1, w.d, device="cuda")
+    lg = torch.zeros(w.T + 1, w.E, device="cuda")
+    y = torch.zeros(w.T + 1, w.d, device="cuda")
+    blob = torch.zeros(mp.moe_prefill_layer_bytes(w.d, w.f, w.E), dtype=torch.uint8, device="cuda")
+    with pytest.raises(mp.MoePrefillError) as ei:
+        mp.moe_prefill_run_layer(h, x, lg, y, weights=blob)          # T > max_tokens
+    assert ei.value.code == mp.MOE_EINVAL
+    with pytest.raises(mp.MoePrefillError) as ei:
+        mp.moe_prefill_run_layer(h, x[:4], lg[:4], y[:4], layer=0)   # no pool configured
+    assert ei.value.code == mp.MOE_ESTATE
+    h.close()
+
+
+def test_lent_workspace():
+    w = wl.WORKLOADS["tiny"]
+    nbytes = mp.moe_prefill_workspace_size(w.d, w.f, w.E, w.k, w.T)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    x = wl.layer_activations(w, 0)
+    lg = wl.layer_logits(w, 0)
+    ex = ExpertCache(w, 0)
+    blob = host_blob(w, ex).cuda()
+    h = mp.moe_prefill_create(w.d, w.f, w.E, w.k, w.T, workspace=ws)
+    g = run_layer_gpu(h, w, x, lg, blob)
+    check_full_parity(w, g, oracle.layer(x, lg, w.k, ex, w.f))
+    h.close()
+    with pytest.raises(mp.MoePrefillError) as ei:
+        mp.moe_prefill_create(w.d, w.f, w.E, w.k, w.T, workspace=ws[: nbytes // 2])
+    assert ei.value.code == mp.MOE_EINVAL
+
+
+def _sampled_case(name, n_tok=24, seed=0):
+    w = wl.WORKLOADS[name]
+    say(f"[case] {w.name} layer 0 (sampled)")
+    x = wl.layer_activations(w, 0)
+    lg = wl.layer_logits(w, 0)
+    blob_ex = ExpertCache(w, 0, keep=False)
+    blob = host_blob(w, blob_ex).cuda()
+    h = make_handle(w)
+    g = run_layer_gpu(h, w, x, lg, blob, exports=("eidx", "weights", "counts", "bounds", "rows", "pos",
+                                                  "xq", "dx", "hq", "dh", "dm"))
+    h.close()
+    del blob
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(seed)
+    eidx, _ = oracle.route(lg, w.k)
+    counts = np.bincount(eidx.reshape(-1), minlength=w.E)
+    big = int(np.argmax(counts))
+    heavy = np.nonzero((eidx == big).any(1))[0]
+    toks = set(rng.choice(w.T, n_tok, replace=False).tolist())
+    toks |= set(heavy[:4].tolist()) | {0, w.T - 1}
+    ref = oracle.layer(x, lg, w.k, ExpertCache(w, 0, keep=False), w.f, tokens=sorted(toks))
+    return w, g, ref
+
+
+def test_biased_48_layer_shape_sampled():
+    w, g, ref = _sampled_case("stream48")
+    check_sampled_parity(w, g, ref)
+
+
+def test_skewed_large_shape_sampled():
+    w, g, ref = _sampled_case("skew", n_tok=16)
+    check_sampled_parity(w, g, ref)
+    assert ref["counts"].max() > 1000 and (ref["counts"] == 0).sum() > 10

@@ -1,0 +1,174 @@
+"""Streamed stacks through the fixed-slot pool: every streamed configuration
+must give outputs identical bit for bit to running the same layers resident
+(the layer-streaming pages' acceptance criterion: matching output hashes with
+and without streaming / pooling), and the prefetch counters must follow the
+rolling-window policy.  Fault hooks force the synchronous fallback and pool
+degradation from the host side; every kernel still runs normally."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_prefill_ffn_amd as mp
+import oracle
+import workload as wl
+from gpu_helpers import ExpertCache, assert_close, assert_equal, host_blob, make_handle, say
+
+pytestmark = pytest.mark.gpu
+
+
+class Stack:
+    def __init__(self, w: wl.Workload, n_layers: int):
+        self.w = w
+        self.n = n_layers
+        self.blobs = [host_blob(w, ExpertCache(w, l, keep=False), pinned=True) for l in range(n_layers)]
+        self.x = [torch.from_numpy(wl.layer_activations(w, l)).cuda() for l in range(n_layers)]
+        self.lg = [torch.from_numpy(wl.layer_logits(w, l)).cuda() for l in range(n_layers)]
+        h = make_handle(w)
+        self.ref = []
+        for l in range(n_layers):
+            dev = self.blobs[l].cuda()
+            y = torch.empty(w.T, w.d, device="cuda")
+            mp.moe_prefill_run_layer(h, self.x[l], self.lg[l], y, layer=-1, weights=dev)
+            torch.cuda.synchronize()
+            self.ref.append(y.cpu().numpy())
+        h.close()
+
+    def run_passes(self, h, passes: int, order=None):
+        order = order or list(range(self.n))
+        outs = []
+        for _ in range(passes):
+            for l in order:
+                y = torch.full((self.w.T, self.w.d), float("nan"), device="cuda")
+                mp.moe_prefill_run_layer(h, self.x[l], self.lg[l], y, layer=l)
+                outs.append((l, y))
+        torch.cuda.synchronize()
+        return [(l, y.cpu().numpy()) for l, y in outs]
+
+    def check(self, outs):
+        for l, y in outs:
+            assert_equal(f"layer {l}", y, self.ref[l])
+
+
+@pytest.fixture(scope="module")
+def tiny5():
+    say("[case] 5-layer tiny stack")
+    return Stack(wl.Workload("stack5_T64_d256_f512_E8_top2", 64, 256, 512, 8, 2, 5, 600), 5)
+
+
+def _configure(h, st, **kw):
+    return mp.stream_pool_configure(h, st.blobs, **kw)
+
+
+def test_rolling_window_depth1_two_slots(tiny5):
+    h = make_handle(tiny5.w)
+    plan = _configure(h, tiny5, prefetch_depth=1, resident_layers=0, requested_slots=2)
+    assert (plan["slots"], plan["depth"], plan["residents"]) == (2, 1, 0)
+    tiny5.check(tiny5.run_passes(h, 2))
+    s = mp.moe_prefill_get_stats(h)
+    # pass 1: layer 0 loads synchronously; every later layer finds its prefetch
+    assert s["sync_loads"] == 1
+    assert s["prefetch_queued"] == 2 * 5
+    assert s["prefetch_activated"] == 2 * 5 - 1
+    assert s["prefetch_failed"] == 0
+    h.close()
+
+
+def test_depth0_is_load_then_compute(tiny5):
+    h = make_handle(tiny5.w)
+    plan = _configure(h, tiny5, prefetch_depth=0, resident_layers=0)
+    assert (plan["slots"], plan["depth"]) == (1, 0)
+    tiny5.check(tiny5.run_passes(h, 2))
+    s = mp.moe_prefill_get_stats(h)
+    assert s["sync_loads"] == 10 and s["prefetch_queued"] == 0
+    h.close()
+
+
+def test_depth2_three_slots_and_residents(tiny5):
+    h = make_handle(tiny5.w)
+    lb = tiny5.blobs[0].numel()
+    slot = (lb + 65535) // 65536 * 65536
+    plan = _configure(h, tiny5, prefetch_depth=2, resident_layers=-1, max_vram_bytes=5 * slot)
+    assert (plan["slots"], plan["depth"], plan["residents"]) == (5, 2, 2)
+    tiny5.check(tiny5.run_passes(h, 3))
+    s = mp.moe_prefill_get_stats(h)
+    assert s["eff_residents"] == 2 and s["prefetch_failed"] == 0
+    # residents never stream: 3 streamed layers per pass after the first
+    assert s["sync_loads"] == 0 or s["sync_loads"] == 1
+    h.close()
+
+
+def test_out_of_order_layers_still_match(tiny5):
+    h = make_handle(tiny5.w)
+    _configure(h, tiny5, prefetch_depth=1, resident_layers=0, requested_slots=2)
+    tiny5.check(tiny5.run_passes(h, 2, order=[3, 1, 4, 4, 0, 2]))
+    h.close()
+
+
+def test_forced_prefetch_failure_falls_back(tiny5):
+    os.environ["MOE_TEST_PREFETCH_FAIL"] = "2"
+    try:
+        h = make_handle(tiny5.w)
+        _configure(h, tiny5, prefetch_depth=1, resident_layers=0, requested_slots=2)
+    finally:
+        del os.environ["MOE_TEST_PREFETCH_FAIL"]
+    tiny5.check(tiny5.run_passes(h, 2))
+    s = mp.moe_prefill_get_stats(h)
+    assert s["prefetch_failed"] == 1
+    assert s["sync_loads"] == 2
+    h.close()
+
+
+def test_pool_degrades_to_one_slot(tiny5):
+    os.environ["MOE_TEST_POOL_MAX_SLOTS"] = "1"
+    try:
+        h = make_handle(tiny5.w)
+        plan = _configure(h, tiny5, prefetch_depth=1, resident_layers=0, requested_slots=2)
+    finally:
+        del os.environ["MOE_TEST_POOL_MAX_SLOTS"]
+    assert (plan["slots"], plan["depth"]) == (1, 0)
+    assert plan["warnings"] & mp.MOE_WARN_POOL_DEGRADED
+    tiny5.check(tiny5.run_passes(h, 2))
+    h.close()
+
+
+def test_one_slot_failure_is_an_error_and_reconfigure_works(tiny5):
+    h = make_handle(tiny5.w)
+    os.environ["MOE_TEST_POOL_FAIL_ALL"] = "1"
+    try:
+        with pytest.raises(mp.MoePrefillError) as ei:
+            _configure(h, tiny5, prefetch_depth=1, resident_layers=0, requested_slots=2)
+    finally:
+        del os.environ["MOE_TEST_POOL_FAIL_ALL"]
+    assert ei.value.code == mp.MOE_ENOMEM
+    with pytest.raises(mp.MoePrefillError) as ei:
+        tiny5.run_passes(h, 1)
+    assert ei.value.code == mp.MOE_ESTATE
+    _configure(h, tiny5, prefetch_depth=1, resident_layers=0, requested_slots=2)
+    tiny5.check(tiny5.run_passes(h, 1))
+    # a new plan releases the old pool first; tearing down works too
+    _configure(h, tiny5, prefetch_depth=2, resident_layers=1, requested_slots=4)
+    tiny5.check(tiny5.run_passes(h, 1))
+    mp.stream_pool_configure(h, [], prefetch_depth=0)
+    h.close()
+
+
+def test_streamed_real_shape_stack_matches_resident_and_oracle():
+    w = wl.WORKLOADS["stream4"]
+    say(f"[case] {w.name}")
+    st = Stack(w, w.n_layers)
+    h = make_handle(w)
+    plan = _configure(h, st, prefetch_depth=w.stream.depth, resident_layers=w.stream.residents,
+                      requested_slots=w.stream.slots)
+    assert (plan["slots"], plan["depth"], plan["residents"]) == (2, 1, 0)
+    outs = st.run_passes(h, 2)
+    st.check(outs)
+    s = mp.moe_prefill_get_stats(h)
+    assert s["bytes_h2d"] == (1 + s["prefetch_queued"]) * st.blobs[0].numel()
+    h.close()
+    # one streamed layer against the oracle too (sampled tokens)
+    toks = [0, 1, 500, 1023]
+    ref = oracle.layer(wl.layer_activations(w, 2), wl.layer_logits(w, 2), w.k, ExpertCache(w, 2, keep=False),
+                       w.f, tokens=toks)
+    assert_close("streamed layer 2 y", outs[2][1][toks], ref["y"])
