@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE prompt (prefill) FFN layer on one MI355X.
+
+One step = one whole layer through the C ABI (route, group, Xq, GU grouped
+GEMM, SwiGLU+requant, down grouped GEMM, combine) on the resident real-shape
+layer: T=1024 tokens, d_model=2048, d_ff=768, E=128 experts, top-8, Q4
+weights resident in HBM, synthetic seeded inputs.  The headline value is
+tokens/s per layer.
+
+Also reported on the same line:
+  roofline      the gate/up grouped GEMM (the dominant kernel): algorithmic
+                int8 ops per launch / its mean device time, measured with HIP
+                events on the launch stream over a timed region of K steps,
+                against the int8 MFMA dense peak (5.0 POPS)
+  kernels       mean device time of every kernel of the layer (same region)
+  streamed      the 4-layer streamed stack (same shape, 2-slot pool, depth-1
+                prefetch): tokens/s per pass, achieved H2D GB/s, measured PCIe
+                GB/s, fraction of copy time hidden and overlap efficiency
+  cpu_baseline  the CPU oracle timed on this host's cores on the same layer
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, published
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("moe_kernels.hip", "moe_kernels.h", "moe_layout.h"):
+        h.update(open(os.path.join(ROOT, "moe_prefill_ffn_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.loads(open(p).read().split("JSON:", 1)[1])
+    except Exception:
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--stream-passes", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-stream", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the MoE prefill FFN path here runs on a single "
+              "MI355X (no layer split, no collectives); run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import moe_prefill_ffn_amd as mp
+    import workload as wl
+
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS["resident"]
+    T, d, f, E, k = w.T, w.d, w.f, w.E, w.k
+    R = T * k
+    log(f"[bench] {w.name}: generating inputs")
+    x = torch.from_numpy(wl.layer_activations(w, 0)).to(dev)
+    lg = torch.from_numpy(wl.layer_logits(w, 0)).to(dev)
+    blob_h = torch.empty(mp.moe_prefill_layer_bytes(d, f, E), dtype=torch.uint8)
+    mp.pack_layer(d, f, E, lambda e: wl.expert_weights(w, 0, e), blob_h)
+    blob = blob_h.to(dev)
+    y = torch.empty(T, d, device=dev)
+    h = mp.moe_prefill_create(d, f, E, k, T, device=0)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mp.moe_prefill_run_layer(h, x, lg, y, layer=-1, weights=blob, stream=stream)
+
+    # ---- headline: K whole layers, inputs resident in HBM
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    value = T / (ms_step * 1e-3)
+    log(f"[bench] {ms_step * 1e3:.1f} us/layer -> {value:,.0f} tokens/s per layer")
+
+    # ---- per-kernel device times (HIP events between the kernels, launch stream)
+    mp.moe_prefill_set_timing(h, True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kt = mp.moe_prefill_kernel_times(h, reset=True)
+    mp.moe_prefill_set_timing(h, False)
+    kern_us = {n: (ms / c * 1e3 if c else None) for n, (c, ms) in kt.items()}
+    gu_us = kern_us["gemm_gate_up"]
+    dn_us = kern_us["gemm_down"]
+    ops_gu = 2.0 * R * (2 * f) * d           # int8 multiply-adds x 2, routed rows only
+    ops_dn = 2.0 * R * d * f
+    gu_tops = ops_gu / (gu_us * 1e-6) / 1e12
+    dn_tops = ops_dn / (dn_us * 1e-6) / 1e12
+    q_bytes = T * d * 4 + T * d + T * (d // 32) * 4
+    c_bytes = R * d * 4 + R * 8 + T * d * 4
+    s_bytes = R * 2 * f * 4 + R * f + R * (f // 32) * 4
+    traffic = load_traffic("gemm_gate_up", "resident")
+    roofline = {
+        "bound": "mfma", "achieved": round(gu_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+        "frac": round(gu_tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
+        "kernel": "gemm_gate_up", "ops_per_launch": ops_gu, "mean_us": round(gu_us, 2),
+        "dtype": "int8 x int4 -> int32 blocks, fp32 epilogue",
+    }
+    kernels = {n: (round(v, 2) if v is not None else None) for n, v in kern_us.items()}
+    hbm = {
+        "quant_x_q8_GBs": round(q_bytes / (kern_us["quant_x_q8"] * 1e-6) / 1e9, 1),
+        "swiglu_q8_GBs": round(s_bytes / (kern_us["swiglu_q8"] * 1e-6) / 1e9, 1),
+        "combine_GBs": round(c_bytes / (kern_us["combine"] * 1e-6) / 1e9, 1),
+        "gemm_down_TOPS": round(dn_tops, 2),
+        "peak_GBs": HBM_PEAK_GBS,
+    }
+    log(f"[bench] kernels (us): {kernels}")
+    log(f"[bench] gate/up GEMM {gu_tops:.1f} TOPS = {100 * gu_tops / INT8_PEAK_TOPS:.2f}% of int8 peak")
+    del blob
+    h.close()
+    torch.cuda.empty_cache()
+
+    line = {
+        "metric": "MoE prefill tokens/s per layer (1 GPU); int8 MFMA %peak; H2D GB/s hidden %",
+        "value": round(value, 1), "unit": "tokens/s per layer", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic (seeded N(0,1) activations/logits, Q4 uniform int4 weights)",
+        "config": {"workload": w.name, "T": T, "d_model": d, "d_ff": f, "n_experts": E, "top_k": k,
+                   "weights": "resident in HBM", "global_batch": T, "seq_len": T, "parallelism": "none"},
+        "roofline": roofline, "kernels_us": kernels, "hbm": hbm,
+    }
+
+    # ---- streamed stack: 4 layers through a 2-slot pool with depth-1 prefetch
+    if not args.no_stream:
+        ws = wl.WORKLOADS["stream4"]
+        log(f"[bench] {ws.name}: packing {ws.n_layers} pinned layer blobs")
+        lb = mp.moe_prefill_layer_bytes(ws.d, ws.f, ws.E)
+        blobs = []
+        for l in range(ws.n_layers):
+            b = torch.empty(lb, dtype=torch.uint8, pin_memory=True)
+            mp.pack_layer(ws.d, ws.f, ws.E, lambda e, l=l: wl.expert_weights(ws, l, e), b)
+            blobs.append(b)
+        xs = [torch.from_numpy(wl.layer_activations(ws, l)).to(dev) for l in range(ws.n_layers)]
+        lgs = [torch.from_numpy(wl.layer_logits(ws, l)).to(dev) for l in range(ws.n_layers)]
+        ys = torch.empty(ws.T, ws.d, device=dev)
+        hs = mp.moe_prefill_create(ws.d, ws.f, ws.E, ws.k, ws.T, device=0)
+        # raw pinned H2D bandwidth (best of 3 over the whole stack)
+        dst = torch.empty(lb, dtype=torch.uint8, device=dev)
+        t_copy = 1e9
+        for _ in range(3):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for b in blobs:
+                dst.copy_(b, non_blocking=True)
+            torch.cuda.synchronize()
+            t_copy = min(t_copy, time.perf_counter() - t0)
+        # compute only: the same layers resident
+        devb = [b.to(dev) for b in blobs]
+        for _ in range(2):
+            for l in range(ws.n_layers):
+                mp.moe_prefill_run_layer(hs, xs[l], lgs[l], ys, layer=-1, weights=devb[l])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.stream_passes):
+            for l in range(ws.n_layers):
+                mp.moe_prefill_run_layer(hs, xs[l], lgs[l], ys, layer=-1, weights=devb[l])
+        torch.cuda.synchronize()
+        t_comp = (time.perf_counter() - t0) / args.stream_passes
+        del devb, dst
+        torch.cuda.empty_cache()
+        plan = mp.stream_pool_configure(hs, blobs, prefetch_depth=ws.stream.depth,
+                                        resident_layers=ws.stream.residents,
+                                        requested_slots=ws.stream.slots)
+        for l in range(ws.n_layers):       # first (cold) pass
+            mp.moe_prefill_run_layer(hs, xs[l], lgs[l], ys, layer=l)
+        torch.cuda.synchronize()
+        s0 = mp.moe_prefill_get_stats(hs)
+        t0 = time.perf_counter()
+        for _ in range(args.stream_passes):
+            for l in range(ws.n_layers):
+                mp.moe_prefill_run_layer(hs, xs[l], lgs[l], ys, layer=l)
+        torch.cuda.synchronize()
+        t_wall = (time.perf_counter() - t0) / args.stream_passes
+        s1 = mp.moe_prefill_get_stats(hs)
+        moved = (s1["bytes_h2d"] - s0["bytes_h2d"]) / args.stream_passes
+        hidden = max(0.0, t_copy + t_comp - t_wall)
+        line["streamed"] = {
+            "workload": ws.name, "layers": ws.n_layers, "slots": plan["slots"], "depth": plan["depth"],
+            "tokens_per_s_per_pass": round(ws.T / t_wall, 1),
+            "ms_per_pass": round(t_wall * 1e3, 3), "ms_per_layer": round(t_wall * 1e3 / ws.n_layers, 3),
+            "h2d_GBs_achieved": round(moved / t_wall / 1e9, 2),
+            "pcie_h2d_GBs_measured": round(ws.n_layers * lb / t_copy / 1e9, 2),
+            "copy_ms_per_pass": round(t_copy * 1e3, 3), "compute_ms_per_pass": round(t_comp * 1e3, 3),
+            "copy_hidden_frac": round(hidden / t_copy, 4),
+            "overlap_efficiency": round(hidden / min(t_copy, t_comp), 4),
+            "prefetch_activated": s1["prefetch_activated"] - s0["prefetch_activated"],
+            "sync_loads": s1["sync_loads"] - s0["sync_loads"],
+        }
+        log(f"[bench] streamed: {line['streamed']}")
+        hs.close()
+        del blobs
+        torch.cuda.empty_cache()
+
+    # ---- CPU oracle on the host's cores, same resident layer (bounded: a few full layers)
+    if not args.no_cpu:
+        import oracle
+        xn = wl.layer_activations(w, 0)
+        ln = wl.layer_logits(w, 0)
+        cache = {e: wl.expert_weights(w, 0, e) for e in range(E)}    # inputs, not timed
+        times = []
+        for _ in range(args.cpu_reps):
+            t0 = time.perf_counter()
+            oracle.layer(xn, ln, k, cache.__getitem__, f)
+            times.append(time.perf_counter() - t0)
+        tc = sorted(times)[len(times) // 2]
+        line["cpu_baseline"] = {
+            "value": round(T / tc, 1), "unit": "tokens/s per layer", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"the full {w.name} layer, {args.cpu_reps} runs, median {tc:.2f} s "
+                      "(expert weights pre-generated, not timed)",
+        }
+        log(f"[bench] cpu oracle: {line['cpu_baseline']}")
+
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -243,6 +243,42 @@ typedef struct moe_stats {
 
 int moe_prefill_get_stats(const moe_prefill_t* h, moe_stats_t* inout);
 
+/* ------------------------------------------------------------- tracing --- */
+
+#define MOE_N_KERNELS 9
+/* Kernel ids, in launch order inside moe_prefill_run_layer. */
+enum {
+    MOE_K_ROUTE = 0,          /* top-k routing + router weights + membership mask */
+    MOE_K_QUANT_X = 1,        /* Xq = Q8(x) */
+    MOE_K_GROUP_PREFIX = 2,   /* per-expert token prefix counts */
+    MOE_K_GROUP_BOUNDS = 3,   /* group bounds + GEMM row tiles */
+    MOE_K_SCATTER = 4,        /* row table */
+    MOE_K_GEMM_GATE_UP = 5,   /* GU grouped GEMM */
+    MOE_K_SWIGLU_Q8 = 6,      /* H = SwiGLU(GU), Hq = Q8(H) */
+    MOE_K_GEMM_DOWN = 7,      /* Dm grouped GEMM */
+    MOE_K_COMBINE = 8         /* y = weighted combine */
+};
+
+typedef struct moe_kernel_times {
+    uint32_t struct_size;
+    int32_t n_kernels;                  /* out: MOE_N_KERNELS */
+    uint64_t launches[MOE_N_KERNELS];   /* out: timed launches per kernel */
+    double total_ms[MOE_N_KERNELS];     /* out: summed device time per kernel */
+} moe_kernel_times_t;
+
+/* enable != 0: every kernel of the following moe_prefill_run_layer calls is
+ * bracketed by HIP events recorded on the launch stream (one event record
+ * between consecutive kernels); 0 stops it.  Host only. */
+int moe_prefill_set_timing(moe_prefill_t* h, int32_t enable);
+
+/* Waits (bounded; MOE_ETIMEOUT) for the timed launches so far, adds their
+ * per-kernel device durations to the handle's totals, writes the totals to
+ * *inout and, if reset != 0, zeroes them. */
+int moe_prefill_kernel_times(moe_prefill_t* h, moe_kernel_times_t* inout, int32_t reset);
+
+/* Name of kernel id (MOE_K_*), or "" for an unknown id. */
+const char* moe_prefill_kernel_name(int32_t id);
+
 #ifdef __cplusplus
 }
 #endif

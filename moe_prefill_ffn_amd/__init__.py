@@ -73,11 +73,20 @@ class moe_stats_t(ctypes.Structure):
                 ("eff_depth", _i32), ("eff_residents", _i32), ("warnings", _i32)]
 
 
+MOE_N_KERNELS = 9
+
+
+class moe_kernel_times_t(ctypes.Structure):
+    _fields_ = [("struct_size", _u32), ("n_kernels", _i32), ("launches", _u64 * MOE_N_KERNELS),
+                ("total_ms", ctypes.c_double * MOE_N_KERNELS)]
+
+
 EXPORTED_SYMBOLS = [
     "moe_prefill_workspace_size", "moe_prefill_create", "moe_prefill_destroy",
     "moe_prefill_last_error", "moe_prefill_expert_bytes", "moe_prefill_layer_bytes",
     "moe_prefill_pack_expert", "moe_prefill_run_layer", "stream_pool_configure",
-    "moe_prefill_plan_pool", "moe_prefill_get_stats",
+    "moe_prefill_plan_pool", "moe_prefill_get_stats", "moe_prefill_set_timing",
+    "moe_prefill_kernel_times", "moe_prefill_kernel_name",
 ]
 
 _lib = None
@@ -107,6 +116,10 @@ def lib():
     L.stream_pool_configure.argtypes = [_vp, ctypes.POINTER(stream_pool_params_t)]
     L.moe_prefill_plan_pool.argtypes = [ctypes.POINTER(moe_pool_plan_t)]
     L.moe_prefill_get_stats.argtypes = [_vp, ctypes.POINTER(moe_stats_t)]
+    L.moe_prefill_set_timing.argtypes = [_vp, _i32]
+    L.moe_prefill_kernel_times.argtypes = [_vp, ctypes.POINTER(moe_kernel_times_t), _i32]
+    L.moe_prefill_kernel_name.argtypes = [_i32]
+    L.moe_prefill_kernel_name.restype = ctypes.c_char_p
     _lib = L
     return L
 
@@ -325,3 +338,21 @@ def moe_prefill_get_stats(handle: Handle) -> dict:
     s.struct_size = ctypes.sizeof(s)
     _check(lib().moe_prefill_get_stats(handle.ptr, ctypes.byref(s)), handle.ptr)
     return {name: getattr(s, name) for name, _ in moe_stats_t._fields_ if name not in ("struct_size", "reserved0")}
+
+
+# --------------------------------------------------------------- tracing ---
+
+def moe_prefill_kernel_name(kernel_id: int) -> str:
+    return lib().moe_prefill_kernel_name(kernel_id).decode()
+
+
+def moe_prefill_set_timing(handle: Handle, enable: bool = True) -> None:
+    _check(lib().moe_prefill_set_timing(handle.ptr, 1 if enable else 0), handle.ptr)
+
+
+def moe_prefill_kernel_times(handle: Handle, reset: bool = True) -> dict:
+    """{kernel name: (launches, total device ms)} of the timed launches so far."""
+    t = moe_kernel_times_t()
+    t.struct_size = ctypes.sizeof(t)
+    _check(lib().moe_prefill_kernel_times(handle.ptr, ctypes.byref(t), 1 if reset else 0), handle.ptr)
+    return {moe_prefill_kernel_name(i): (int(t.launches[i]), float(t.total_ms[i])) for i in range(t.n_kernels)}

@@ -9,7 +9,7 @@ namespace moe {
 struct GemmArgs {
     const int8_t* A;          // activation codes [rows, K]
     const float* A_scale;     // their block scales [rows, K/32]
-    const int32_t* row_src;   // grouped row -> A row (nullptr: identity)
+    const int32_t* row_src;   // grouped row -> A row (gate/up launch; the down launch reads row r)
     const uint8_t* blob;      // layer weight blob
     uint64_t expert_stride;   // bytes per expert
     uint64_t q_off, s_off;    // matrix quant / scale section offsets in an expert
@@ -17,7 +17,7 @@ struct GemmArgs {
     const int32_t* ntiles;    // number of valid tiles (device)
     float* out;               // [R, N]
     int N, K;
-    int gu_f;                 // f for the interleaved gate/up matrix, 0 otherwise
+    int gu_f;                 // f of the interleaved gate/up matrix (gate/up launch only)
 };
 
 struct LayerLaunch {
@@ -45,7 +45,13 @@ struct LayerLaunch {
     float* dh;
     float* dm;
     float* h_out;             // optional export of H (nullptr: not written)
+    hipEvent_t* marks;        // optional: kNumKernels + 1 timing events (nullptr: none);
+                              // marks[i] before kernel i, marks[kNumKernels] after the last
 };
+
+// kernel ids in launch order (timing)
+enum KernelId { kRoute, kQuantX, kGroupPrefix, kGroupBounds, kScatter, kGemmGateUp, kSwigluQ8,
+                kGemmDown, kCombine, kNumKernels };
 
 // route, quantise X, group, scatter, GU GEMM, SwiGLU+Q8, down GEMM (last reader
 // of the weights) -- everything up to the combine.

@@ -334,7 +334,8 @@ __device__ __forceinline__ uint32_t nib_to_i8(uint32_t v)   // 4 offset-binary n
     return (v + 0x78787878u) ^ 0x80808080u;
 }
 
-__global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs g)
+template <bool kGateUp>
+__device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
 {
     const int tile = blockIdx.y;
     if (tile >= *g.ntiles) return;   // uniform across the workgroup
@@ -359,7 +360,7 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs g)
         const int idx = i * 256 + tid;
         const int row = idx >> 4;
         const int r = r0 + (row < nrows ? row : 0);
-        const int src = g.row_src ? g.row_src[r] : r;
+        const int src = kGateUp ? g.row_src[r] : r;
         a_src[i] = row < nrows ? g.A + (int64_t)src * K : nullptr;
         a_col[i] = (idx & 15) * 16;
         a_lds[i] = row * kAPitch + a_col[i];
@@ -369,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs g)
     const float* s_src = nullptr;
     if (s_row < nrows) {
         const int r = r0 + s_row;
-        const int src = g.row_src ? g.row_src[r] : r;
+        const int src = kGateUp ? g.row_src[r] : r;
         s_src = g.A_scale + (int64_t)src * nbk;
     }
 
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs g)
 
     if (!wave_on) return;
     const int j = lane & 31;
-    const int col = g.gu_f ? gu_logical_row(nt, j, g.gu_f) : nt * 32 + j;
+    const int col = kGateUp ? gu_logical_row(nt, j, g.gu_f) : nt * 32 + j;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
 #pragma unroll
@@ -508,6 +509,12 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs g)
         }
     }
 }
+
+// gate/up projection: A rows gathered from Xq through the row table, output
+// columns in logical gate | up order.
+__global__ __launch_bounds__(256, 2) void k_gemm_gate_up(GemmArgs g) { grouped_gemm_body<true>(g); }
+// down projection: A = Hq in row-table order.
+__global__ __launch_bounds__(256, 2) void k_gemm_down(GemmArgs g) { grouped_gemm_body<false>(g); }
 
 // -------------------------------------------------------------- combine ---
 // y[t, :] = sum_j w[t, j] * dm[pos[t*k + j], :], j ascending, fma chain from 0.
@@ -547,18 +554,28 @@ __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, int6
 // ------------------------------------------------------------- launches ---
 static inline unsigned nblk(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
 
+static inline void mark(const LayerLaunch& L, int i, hipStream_t st)
+{
+    if (L.marks) (void)hipEventRecord(L.marks[i], st);
+}
+
 hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
 {
     const int64_t R = (int64_t)L.T * L.k;
+    mark(L, 0, st);
     hipLaunchKernelGGL(k_route, dim3(nblk(L.T, 4)), dim3(256), 0, st, L.logits, L.T, L.E, L.k,
                        L.eidx, L.wts, L.mask, L.W);
     const int64_t xblocks = (int64_t)L.T * (L.d / 32);
+    mark(L, 1, st);
     hipLaunchKernelGGL(k_quant_q8, dim3(nblk(xblocks * 8, 256)), dim3(256), 0, st, L.x, xblocks,
                        L.xq, L.dx);
+    mark(L, 2, st);
     hipLaunchKernelGGL(k_group_prefix, dim3(L.E), dim3(256), 0, st, L.mask, L.W, L.wprefix,
                        L.counts);
+    mark(L, 3, st);
     hipLaunchKernelGGL(k_group_bounds, dim3(1), dim3(1024), 0, st, L.counts, L.E, L.bounds, L.tiles,
                        L.ntiles);
+    mark(L, 4, st);
     hipLaunchKernelGGL(k_scatter, dim3(nblk(R, 256)), dim3(256), 0, st, L.eidx, R, L.k, L.mask,
                        L.wprefix, L.bounds, L.W, L.rows, L.pos, L.rtok);
     const int max_tiles_now = (int)((R + kBM - 1) / kBM) + (L.E < R ? L.E : (int)R);
@@ -577,9 +594,11 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     gu.N = 2 * L.f;
     gu.K = L.d;
     gu.gu_f = L.f;
-    hipLaunchKernelGGL(k_grouped_gemm, dim3(nblk(gu.N / 32, 4), max_tiles_now), dim3(256), 0, st, gu);
+    mark(L, 5, st);
+    hipLaunchKernelGGL(k_gemm_gate_up, dim3(nblk(gu.N / 32, 4), max_tiles_now), dim3(256), 0, st, gu);
 
     const int64_t hblocks = R * (L.f / 32);
+    mark(L, 6, st);
     hipLaunchKernelGGL(k_swiglu_q8, dim3(nblk(hblocks * 8, 256)), dim3(256), 0, st, L.gu, R, L.f,
                        L.hq, L.dh, L.h_out);
 
@@ -593,7 +612,9 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     dn.N = L.d;
     dn.K = L.f;
     dn.gu_f = 0;
-    hipLaunchKernelGGL(k_grouped_gemm, dim3(nblk(dn.N / 32, 4), max_tiles_now), dim3(256), 0, st, dn);
+    mark(L, 7, st);
+    hipLaunchKernelGGL(k_gemm_down, dim3(nblk(dn.N / 32, 4), max_tiles_now), dim3(256), 0, st, dn);
+    mark(L, 8, st);
     return hipGetLastError();
 }
 
@@ -603,6 +624,7 @@ hipError_t launch_combine(const LayerLaunch& L, hipStream_t st)
     const int64_t mw = (int64_t)L.E * L.W;
     hipLaunchKernelGGL(k_combine, dim3(nblk(work > mw ? work : mw, 256)), dim3(256), 0, st, L.dm,
                        L.wts, L.pos, L.T, L.k, L.d, L.y, L.mask, mw);
+    mark(L, 9, st);
     return hipGetLastError();
 }
 

@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <array>
 #include <chrono>
 #include <string>
 #include <thread>
@@ -50,6 +51,12 @@ struct moe_prefill {
     uint64_t fail_at = 0;   // test hook: this prefetch enqueue (1-based) is treated as failed
 
     moe_stats_t stats{};
+
+    // kernel timing
+    bool timing = false;
+    std::vector<std::array<hipEvent_t, kNumKernels + 1>> t_pending, t_free;
+    uint64_t t_launches[kNumKernels] = {};
+    double t_ms[kNumKernels] = {};
 };
 
 static thread_local std::string g_err;
@@ -375,6 +382,9 @@ void moe_prefill_destroy(moe_prefill_t* h)
     {
         DevGuard guard(h->dev);
         pool_release(h);
+        for (auto* v : {&h->t_pending, &h->t_free})
+            for (auto& set : *v)
+                for (hipEvent_t e : set) (void)hipEventDestroy(e);
         if (h->copy) (void)hipStreamDestroy(h->copy);
         if (h->ws_owned && h->ws) (void)hipFree(h->ws);
     }
@@ -467,6 +477,20 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
     LL.dh = reinterpret_cast<float*>(w + h->L.dh);
     LL.dm = reinterpret_cast<float*>(w + h->L.dm);
     LL.h_out = io.h;
+    LL.marks = nullptr;
+    std::array<hipEvent_t, kNumKernels + 1> tset{};
+    if (h->timing) {
+        if (!h->t_free.empty()) {
+            tset = h->t_free.back();
+            h->t_free.pop_back();
+        } else {
+            for (auto& ev : tset) {
+                e = hipEventCreate(&ev);
+                if (e != hipSuccess) return hip_fail(h, e, "timing events");
+            }
+        }
+        LL.marks = tset.data();
+    }
 
     e = launch_layer(LL, st);
     if (e != hipSuccess) {
@@ -487,6 +511,7 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
         h->mask_dirty = true;
         return hip_fail(h, e, "combine launch");
     }
+    if (h->timing) h->t_pending.push_back(tset);
 
     // optional exports of the intermediate buffers
     const uint64_t R = (uint64_t)T * h->k;
@@ -681,6 +706,54 @@ int stream_pool_configure(moe_prefill_t* h, stream_pool_params_t* inout)
     h->stats.warnings = warn;
     write_struct(inout, p);
     h->err.clear();
+    return MOE_OK;
+}
+
+int moe_prefill_set_timing(moe_prefill_t* h, int32_t enable)
+{
+    if (!h) return fail(nullptr, MOE_EINVAL, "null handle");
+    h->timing = enable != 0;
+    return MOE_OK;
+}
+
+const char* moe_prefill_kernel_name(int32_t id)
+{
+    static const char* names[kNumKernels] = {"route_topk", "quant_x_q8", "group_prefix",
+                                             "group_bounds", "row_scatter", "gemm_gate_up",
+                                             "swiglu_q8", "gemm_down", "combine"};
+    return (id >= 0 && id < kNumKernels) ? names[id] : "";
+}
+
+int moe_prefill_kernel_times(moe_prefill_t* h, moe_kernel_times_t* inout, int32_t reset)
+{
+    if (!h) return fail(nullptr, MOE_EINVAL, "null handle");
+    moe_kernel_times_t out;
+    std::string why;
+    if (!read_struct(inout, &out, &why)) return fail(h, MOE_EINVAL, why);
+    DevGuard guard(h->dev);
+    for (auto& set : h->t_pending) {
+        const int rc = wait_event(h, set[kNumKernels]);
+        if (rc != MOE_OK) return rc;
+        for (int i = 0; i < kNumKernels; ++i) {
+            float ms = 0.0f;
+            if (hipEventElapsedTime(&ms, set[i], set[i + 1]) == hipSuccess) {
+                h->t_ms[i] += ms;
+                h->t_launches[i]++;
+            }
+        }
+        h->t_free.push_back(set);
+    }
+    h->t_pending.clear();
+    out.n_kernels = kNumKernels;
+    for (int i = 0; i < kNumKernels; ++i) {
+        out.launches[i] = h->t_launches[i];
+        out.total_ms[i] = h->t_ms[i];
+        if (reset) {
+            h->t_launches[i] = 0;
+            h->t_ms[i] = 0.0;
+        }
+    }
+    write_struct(inout, out);
     return MOE_OK;
 }
 
