@@ -71,6 +71,8 @@ def main() -> int:
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 256 MiB device-to-device copies (counter scale reference)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the MoE prefill FFN path here runs on a single "
@@ -84,6 +86,15 @@ def main() -> int:
     import workload as wl
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        # a plain copy of known size: reads and writes exactly 256 MiB per launch
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": src.numel() * 4, "launches": 5}))
+        return 0
     w = wl.WORKLOADS["resident"]
     T, d, f, E, k = w.T, w.d, w.f, w.E, w.k
     R = T * k

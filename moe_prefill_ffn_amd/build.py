@@ -20,6 +20,7 @@ FLAGS = [
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
+    "-Wno-inline-asm",   # M0 is clobbered on purpose by the direct-to-LDS loads (no compiler use of M0 there)
 ]
 
 

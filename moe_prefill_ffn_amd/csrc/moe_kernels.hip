@@ -321,100 +321,132 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
 // for the rows r of each row tile (all of one expert e).
 //
 // Workgroup = 4 waves = one row tile (64 rows) x 4 weight n-tiles (128 output
-// columns); wave w owns n-tile 4*blockIdx.x + w for all 64 rows (two 32x32
-// MFMA tiles stacked along M, sharing the unpacked B operand).  The gathered
-// A rows and their block scales are staged through LDS 256 K-bytes (8 blocks)
-// at a time, double buffered; each wave streams its own packed Q4 weights
-// straight from global memory (one 16-byte coalesced load per K pair).
-constexpr int kStageK = 256;            // K bytes per LDS stage
-constexpr int kAPitch = kStageK + 16;   // padded LDS row pitch
+// columns); wave w owns n-tile 4*ng + w for all 64 rows: two 32x32 tiles
+// stacked along M that share the unpacked B operand.
+//
+// K advances one packed pair (2 blocks, 64 K) per stage through a 4-deep LDS
+// ring filled by direct global->LDS loads (no register staging), issued three
+// stages ahead.  Per stage and wave exactly three loads: 1 KiB of gathered A
+// rows, the wave's 1 KiB of packed Q4 weights, and 256 B holding the wave's
+// fp16 weight scales (lanes 0-31) and the A block scales of 16 rows (lanes
+// 32-63).  A is stored as 128-byte "super-rows" (two 64-byte rows) whose
+// 16-byte chunks are XOR-swizzled by the super-row index, which makes the MFMA
+// operand reads bank-conflict free.
+//
+// Per 32-block the matrix cores do all products: two v_mfma_i32_32x32x32_i8
+// give the exact int32 block sums of both row halves, and one
+// v_mfma_f32_32x32x1_2b_f32 gives the rank-1 scale products
+// a_scale[row] * w_scale[col] of both halves (one rounding each, as a plain
+// fp32 multiply).  The VALU is left with convert + fma per element.
+//
+// Workgroups are numbered so that each XCD (dispatch is round-robin over the
+// 8 XCDs) receives a contiguous run of tiles: the n-groups of a row tile and
+// the row tiles of an expert share that XCD's L2.
+constexpr int kRing = 4;                  // LDS stages in flight
+constexpr int kA_OFF = 0;                 // [32 super-rows][8 chunks of 16 B], swizzled
+constexpr int kB_OFF = 4096;              // [4 waves][64 lanes][16 B]
+constexpr int kSX_OFF = 8192;             // [4 waves][ {32 cols x 2 fp16} | {16 rows x 2 fp32} ]
+constexpr int kStageBytes = 9216;
+
+typedef float v32f __attribute__((ext_vector_type(32)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 __device__ __forceinline__ uint32_t nib_to_i8(uint32_t v)   // 4 offset-binary nibbles -> 4 int8
 {
     return (v + 0x78787878u) ^ 0x80808080u;
 }
 
+// Direct global->LDS loads: lane i's 16 (or 4) bytes from g land at LDS
+// wave_base + 16 i (4 i).  Issued as inline asm so the compiler's wait-count
+// bookkeeping does not track them: the ring below waits for them explicitly
+// (vmcnt) and never lets the compiler drain loads still meant to be in flight.
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
+__device__ __forceinline__ void g2lds16(const void* g, const uint8_t* wave_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(lds_addr(wave_base)) : "memory", "m0");
+}
+__device__ __forceinline__ void g2lds4(const void* g, const uint8_t* wave_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(g), "s"(lds_addr(wave_base)) : "memory", "m0");
+}
+
+// byte offset of (row r, 16-byte chunk c < 4) of a stage's A tile
+__device__ __forceinline__ int a_lds_off(int r, int c)
+{
+    const int sr = r >> 1;
+    return sr * 128 + ((((r & 1) << 2) | c) ^ (sr & 7)) * 16;
+}
+
 template <bool kGateUp>
 __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
 {
-    const int tile = blockIdx.y;
-    if (tile >= *g.ntiles) return;   // uniform across the workgroup
+    const int NG = ((g.N >> 5) + 3) >> 2;                 // n-groups of 4 n-tiles
+    const int n_act = *g.ntiles * NG;
+    const int L = blockIdx.x;
+    if (L >= n_act) return;                               // uniform across the workgroup
+    const int q8 = n_act >> 3, r8 = n_act & 7, xcd = L & 7, slot = L >> 3;
+    const int tau = xcd < r8 ? xcd * (q8 + 1) + slot : r8 * (q8 + 1) + (xcd - r8) * q8 + slot;
+    const int tile = tau / NG, ng = tau - tile * NG;
+
     const int e = g.tiles[3 * tile + 0];
     const int r0 = g.tiles[3 * tile + 1];
-    const int nrows = g.tiles[3 * tile + 2] - r0;   // 1 .. kBM
+    const int nrows = g.tiles[3 * tile + 2] - r0;          // 1 .. kBM
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = g.K, N = g.N;
     const int nbk = K >> 5, npairs = K >> 6;
-    const int nt = blockIdx.x * 4 + wave;
-    const bool wave_on = nt < (N >> 5);
-    const int nstages = (K + kStageK - 1) / kStageK;
+    const int nt_real = ng * 4 + wave;
+    const bool wave_on = nt_real < (N >> 5);
+    const int nt = wave_on ? nt_real : (N >> 5) - 1;      // idle waves load valid memory
 
-    __shared__ __attribute__((aligned(16))) int8_t sA[2][kBM * kAPitch];
-    __shared__ __attribute__((aligned(16))) float sS[2][8][kBM];
+    // ring of four LDS stage slots (the loop below is unrolled over the slots)
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring2[kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring3[kStageBytes];
 
-    // ---- per-thread A fill assignment: 4 x 16 bytes, rows (idx >> 4), col (idx & 15) * 16
-    const int8_t* a_src[4];
-    int a_lds[4], a_col[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = i * 256 + tid;
-        const int row = idx >> 4;
-        const int r = r0 + (row < nrows ? row : 0);
-        const int src = kGateUp ? g.row_src[r] : r;
-        a_src[i] = row < nrows ? g.A + (int64_t)src * K : nullptr;
-        a_col[i] = (idx & 15) * 16;
-        a_lds[i] = row * kAPitch + a_col[i];
+    // ---- load sources (all addresses clamped in bounds)
+    // A: this wave fills super-rows 8w..8w+7, lane -> super-row 8w + lane/8, slot lane%8
+    const int8_t* a_src;
+    int a_col;
+    {
+        const int sr = 8 * wave + (lane >> 3);
+        const int cis = (lane & 7) ^ (sr & 7);             // chunk-in-super-row held by this slot
+        const int row = 2 * sr + (cis >> 2);
+        const int rr = r0 + (row < nrows ? row : nrows - 1);
+        const int src = kGateUp ? g.row_src[rr] : rr;
+        a_src = g.A + (int64_t)src * K;
+        a_col = (cis & 3) * 16;
     }
-    // scales fill: thread -> row tid >> 2, blocks 2*(tid & 3) and +1 of the stage
-    const int s_row = tid >> 2, s_b = (tid & 3) * 2;
-    const float* s_src = nullptr;
-    if (s_row < nrows) {
-        const int r = r0 + s_row;
-        const int src = kGateUp ? g.row_src[r] : r;
-        s_src = g.A_scale + (int64_t)src * nbk;
-    }
-
-    // ---- this wave's weight stream
+    // scales: lanes 0-31 -> fp16 pair scales of weight column lane, lanes 32-63 -> A block
+    // scales of row 16w + (lane-32)/2, block (lane & 1) of the pair
     const uint8_t* ex = g.blob + (uint64_t)e * g.expert_stride;
-    const uint4* wq = reinterpret_cast<const uint4*>(ex + g.q_off) + (int64_t)nt * npairs * 64 + lane;
-    const uint32_t* ws = reinterpret_cast<const uint32_t*>(ex + g.s_off) + (int64_t)nt * npairs * 32 + (lane & 31);
+    const uint8_t* wq = ex + g.q_off + (uint64_t)nt * npairs * 1024 + lane * 16;
+    const uint8_t* sx_src;
+    int sx_step;
+    if (lane < 32) {
+        sx_src = ex + g.s_off + (uint64_t)nt * npairs * 128 + lane * 4;
+        sx_step = 128;
+    } else {
+        const int row = 16 * wave + ((lane - 32) >> 1);
+        const int rr = r0 + (row < nrows ? row : nrows - 1);
+        const int src = kGateUp ? g.row_src[rr] : rr;
+        sx_src = reinterpret_cast<const uint8_t*>(g.A_scale + (int64_t)src * nbk + (lane & 1));
+        sx_step = 8;
+    }
 
-    uint4 a_reg[4];
-    float2 s_reg;
-    uint4 bq_cur[4], bq_nxt[4];
-    uint32_t bs_cur[4], bs_nxt[4];
-
-    auto load_a = [&](int stage) {
-        const int k0 = stage * kStageK;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (a_src[i] && k0 + a_col[i] < K)
-                a_reg[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0 + a_col[i]);
-            else
-                a_reg[i] = make_uint4(0, 0, 0, 0);
-        }
-        const int b0 = stage * 8 + s_b;
-        s_reg.x = (s_src && b0 < nbk) ? s_src[b0] : 0.0f;
-        s_reg.y = (s_src && b0 + 1 < nbk) ? s_src[b0 + 1] : 0.0f;
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sA[buf][a_lds[i]]) = a_reg[i];
-        sS[buf][s_b][s_row] = s_reg.x;
-        sS[buf][s_b + 1][s_row] = s_reg.y;
-    };
-    auto load_b = [&](int stage, uint4* bq, uint32_t* bs) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int pr = stage * 4 + p;
-            if (wave_on && pr < npairs) {
-                bq[p] = wq[(int64_t)pr * 64];
-                bs[p] = ws[(int64_t)pr * 32];
-            } else {
-                bq[p] = make_uint4(0, 0, 0, 0);
-                bs[p] = 0;
-            }
-        }
+    // stage = packed pair pr (clamped: tail stages reload the last pair, never read)
+    auto issue = [&](int pr, uint8_t* sb) {
+        const int p = pr < npairs ? pr : npairs - 1;
+        g2lds16(a_src + p * 64 + a_col, sb + kA_OFF + wave * 1024);
+        g2lds16(wq + (uint64_t)p * 1024, sb + kB_OFF + wave * 1024);
+        g2lds4(sx_src + (uint64_t)p * sx_step, sb + kSX_OFF + wave * 256);
     };
 
     float acc0[16], acc1[16];
@@ -424,81 +456,69 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
         acc1[i] = 0.0f;
     }
     const bool two = nrows > 32;
-    const int h = lane >> 5;
+    const int h = lane >> 5, j32 = lane & 31;
     const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    v32f fzero;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) fzero[i] = 0.0f;
+    // A-operand offsets (chunk index depends on the block of the pair: 2*q + h)
+    const int a_off0[2] = {a_lds_off(j32, h), a_lds_off(j32, 2 + h)};
+    const int a_off1[2] = {a_lds_off(32 + j32, h), a_lds_off(32 + j32, 2 + h)};
+    // this lane's A scales (row = lane) live in wave (lane/16)'s scale region
+    const int x_off = kSX_OFF + (lane >> 4) * 256 + 128 + (lane & 15) * 8;
 
-    load_a(0);
-    load_b(0, bq_cur, bs_cur);
-    store_a(0);
-
-    for (int s = 0; s < nstages; ++s) {
-        const int buf = s & 1;
-        __syncthreads();
-        const bool more = s + 1 < nstages;
-        if (more) {
-            load_a(s + 1);
-            load_b(s + 1, bq_nxt, bs_nxt);
-        }
-        if (wave_on) {
-            const int pairs_here = npairs - s * 4 < 4 ? npairs - s * 4 : 4;
+    // one stage: wait for its loads, sync, queue the stage three ahead into the
+    // slot freed by the previous stage, then two blocks of MFMA + epilogue
+    auto stage = [&](int s, const uint8_t* sb, uint8_t* sb_next3) {
+        // this wave's stage-s loads have landed (stages s+1, s+2 may still fly), then
+        // everyone's have, and stage s-1 is fully read so its slot can be refilled
+        asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+        issue(s + kRing - 1, sb_next3);
+        if (!wave_on) return;
+        const uint4 bq = *reinterpret_cast<const uint4*>(sb + kB_OFF + wave * 1024 + lane * 16);
+        const uint32_t bs = *reinterpret_cast<const uint32_t*>(sb + kSX_OFF + wave * 256 + j32 * 4);
+        const float2 dx = *reinterpret_cast<const float2*>(sb + x_off);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                if (p < pairs_here) {
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t w0 = q ? bq.z : bq.x;
+            const uint32_t w1 = q ? bq.w : bq.y;
+            v4i bop;
+            bop.x = (int)nib_to_i8(w0 & 0x0F0F0F0Fu);
+            bop.y = (int)nib_to_i8((w0 >> 4) & 0x0F0F0F0Fu);
+            bop.z = (int)nib_to_i8(w1 & 0x0F0F0F0Fu);
+            bop.w = (int)nib_to_i8((w1 >> 4) & 0x0F0F0F0Fu);
+            const uint16_t hb = (uint16_t)(q ? (bs >> 16) : (bs & 0xffffu));
+            const float dw = (float)__builtin_bit_cast(_Float16, hb);
+            // t[16*half + i] = a_scale(row of D element i in that half) * w_scale(col)
+            const v32f t = __builtin_amdgcn_mfma_f32_32x32x1f32(q ? dx.y : dx.x, dw, fzero, 0, 0, 0);
+            {
+                const v4i a = *reinterpret_cast<const v4i*>(sb + kA_OFF + a_off0[q]);
+                const v16i is = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop, zero, 0, 0, 0);
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const int bl = 2 * p + q;
-                        const uint32_t w0 = q ? bq_cur[p].z : bq_cur[p].x;
-                        const uint32_t w1 = q ? bq_cur[p].w : bq_cur[p].y;
-                        v4i bop;
-                        bop.x = (int)nib_to_i8(w0 & 0x0F0F0F0Fu);
-                        bop.y = (int)nib_to_i8((w0 >> 4) & 0x0F0F0F0Fu);
-                        bop.z = (int)nib_to_i8(w1 & 0x0F0F0F0Fu);
-                        bop.w = (int)nib_to_i8((w1 >> 4) & 0x0F0F0F0Fu);
-                        const uint16_t hb = (uint16_t)(q ? (bs_cur[p] >> 16) : (bs_cur[p] & 0xffffu));
-                        const float dw = (float)__builtin_bit_cast(_Float16, hb);
-                        {
-                            const v4i a = *reinterpret_cast<const v4i*>(
-                                &sA[buf][(lane & 31) * kAPitch + bl * 32 + h * 16]);
-                            const v16i is = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop, zero, 0, 0, 0);
+                for (int i = 0; i < 16; ++i) acc0[i] = __builtin_fmaf((float)is[i], t[i], acc0[i]);
+            }
+            if (two) {
+                const v4i a = *reinterpret_cast<const v4i*>(sb + kA_OFF + a_off1[q]);
+                const v16i is = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop, zero, 0, 0, 0);
 #pragma unroll
-                            for (int gq = 0; gq < 4; ++gq) {
-                                const float4 dx = *reinterpret_cast<const float4*>(&sS[buf][bl][8 * gq + 4 * h]);
-                                acc0[4 * gq + 0] = __builtin_fmaf((float)is[4 * gq + 0], dx.x * dw, acc0[4 * gq + 0]);
-                                acc0[4 * gq + 1] = __builtin_fmaf((float)is[4 * gq + 1], dx.y * dw, acc0[4 * gq + 1]);
-                                acc0[4 * gq + 2] = __builtin_fmaf((float)is[4 * gq + 2], dx.z * dw, acc0[4 * gq + 2]);
-                                acc0[4 * gq + 3] = __builtin_fmaf((float)is[4 * gq + 3], dx.w * dw, acc0[4 * gq + 3]);
-                            }
-                        }
-                        if (two) {
-                            const v4i a = *reinterpret_cast<const v4i*>(
-                                &sA[buf][(32 + (lane & 31)) * kAPitch + bl * 32 + h * 16]);
-                            const v16i is = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop, zero, 0, 0, 0);
-#pragma unroll
-                            for (int gq = 0; gq < 4; ++gq) {
-                                const float4 dx = *reinterpret_cast<const float4*>(&sS[buf][bl][32 + 8 * gq + 4 * h]);
-                                acc1[4 * gq + 0] = __builtin_fmaf((float)is[4 * gq + 0], dx.x * dw, acc1[4 * gq + 0]);
-                                acc1[4 * gq + 1] = __builtin_fmaf((float)is[4 * gq + 1], dx.y * dw, acc1[4 * gq + 1]);
-                                acc1[4 * gq + 2] = __builtin_fmaf((float)is[4 * gq + 2], dx.z * dw, acc1[4 * gq + 2]);
-                                acc1[4 * gq + 3] = __builtin_fmaf((float)is[4 * gq + 3], dx.w * dw, acc1[4 * gq + 3]);
-                            }
-                        }
-                    }
-                }
+                for (int i = 0; i < 16; ++i) acc1[i] = __builtin_fmaf((float)is[i], t[16 + i], acc1[i]);
             }
         }
-        if (more) {
-            store_a(buf ^ 1);
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                bq_cur[p] = bq_nxt[p];
-                bs_cur[p] = bs_nxt[p];
-            }
-        }
+    };
+
+    issue(0, ring0);
+    issue(1, ring1);
+    issue(2, ring2);
+    for (int s = 0; s < npairs; s += kRing) {
+        stage(s, ring0, ring3);
+        if (s + 1 < npairs) stage(s + 1, ring1, ring0);
+        if (s + 2 < npairs) stage(s + 2, ring2, ring1);
+        if (s + 3 < npairs) stage(s + 3, ring3, ring2);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped tail loads before exit
 
     if (!wave_on) return;
-    const int j = lane & 31;
-    const int col = kGateUp ? gu_logical_row(nt, j, g.gu_f) : nt * 32 + j;
+    const int col = kGateUp ? gu_logical_row(nt, j32, g.gu_f) : nt * 32 + j32;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
 #pragma unroll
@@ -512,9 +532,9 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
 
 // gate/up projection: A rows gathered from Xq through the row table, output
 // columns in logical gate | up order.
-__global__ __launch_bounds__(256, 2) void k_gemm_gate_up(GemmArgs g) { grouped_gemm_body<true>(g); }
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm_gate_up(GemmArgs g) { grouped_gemm_body<true>(g); }
 // down projection: A = Hq in row-table order.
-__global__ __launch_bounds__(256, 2) void k_gemm_down(GemmArgs g) { grouped_gemm_body<false>(g); }
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm_down(GemmArgs g) { grouped_gemm_body<false>(g); }
 
 // -------------------------------------------------------------- combine ---
 // y[t, :] = sum_j w[t, j] * dm[pos[t*k + j], :], j ascending, fma chain from 0.
@@ -595,7 +615,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     gu.K = L.d;
     gu.gu_f = L.f;
     mark(L, 5, st);
-    hipLaunchKernelGGL(k_gemm_gate_up, dim3(nblk(gu.N / 32, 4), max_tiles_now), dim3(256), 0, st, gu);
+    hipLaunchKernelGGL(k_gemm_gate_up, dim3(nblk(gu.N / 32, 4) * max_tiles_now), dim3(256), 0, st, gu);
 
     const int64_t hblocks = R * (L.f / 32);
     mark(L, 6, st);
@@ -613,7 +633,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     dn.K = L.f;
     dn.gu_f = 0;
     mark(L, 7, st);
-    hipLaunchKernelGGL(k_gemm_down, dim3(nblk(dn.N / 32, 4), max_tiles_now), dim3(256), 0, st, dn);
+    hipLaunchKernelGGL(k_gemm_down, dim3(nblk(dn.N / 32, 4) * max_tiles_now), dim3(256), 0, st, dn);
     mark(L, 8, st);
     return hipGetLastError();
 }
