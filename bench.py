@@ -138,7 +138,7 @@ def main() -> int:
     ops_dn = 2.0 * R * d * f
     gu_tops = ops_gu / (gu_us * 1e-6) / 1e12
     dn_tops = ops_dn / (dn_us * 1e-6) / 1e12
-    q_bytes = T * d * 4 + T * d + T * (d // 32) * 4
+    q_bytes = T * E * 4 + R * 8 + T * d * 4 + T * d + T * (d // 32) * 4   # logits, eidx+w, X, Xq, dx
     c_bytes = R * d * 4 + R * 8 + T * d * 4
     s_bytes = R * 2 * f * 4 + R * f + R * (f // 32) * 4
     traffic = load_traffic("gemm_gate_up", "resident")
@@ -150,7 +150,7 @@ def main() -> int:
     }
     kernels = {n: (round(v, 2) if v is not None else None) for n, v in kern_us.items()}
     hbm = {
-        "quant_x_q8_GBs": round(q_bytes / (kern_us["quant_x_q8"] * 1e-6) / 1e9, 1),
+        "route_quant_GBs": round(q_bytes / (kern_us["route_quant"] * 1e-6) / 1e9, 1),
         "swiglu_q8_GBs": round(s_bytes / (kern_us["swiglu_q8"] * 1e-6) / 1e9, 1),
         "combine_GBs": round(c_bytes / (kern_us["combine"] * 1e-6) / 1e9, 1),
         "gemm_down_TOPS": round(dn_tops, 2),

@@ -245,18 +245,16 @@ int moe_prefill_get_stats(const moe_prefill_t* h, moe_stats_t* inout);
 
 /* ------------------------------------------------------------- tracing --- */
 
-#define MOE_N_KERNELS 9
+#define MOE_N_KERNELS 7
 /* Kernel ids, in launch order inside moe_prefill_run_layer. */
 enum {
-    MOE_K_ROUTE = 0,          /* top-k routing + router weights + membership mask */
-    MOE_K_QUANT_X = 1,        /* Xq = Q8(x) */
-    MOE_K_GROUP_PREFIX = 2,   /* per-expert token prefix counts */
-    MOE_K_GROUP_BOUNDS = 3,   /* group bounds + GEMM row tiles */
-    MOE_K_SCATTER = 4,        /* row table */
-    MOE_K_GEMM_GATE_UP = 5,   /* GU grouped GEMM */
-    MOE_K_SWIGLU_Q8 = 6,      /* H = SwiGLU(GU), Hq = Q8(H) */
-    MOE_K_GEMM_DOWN = 7,      /* Dm grouped GEMM */
-    MOE_K_COMBINE = 8         /* y = weighted combine */
+    MOE_K_ROUTE_QUANT = 0,    /* top-k routing, router weights, membership mask; Xq = Q8(x) */
+    MOE_K_GROUP = 1,          /* counts, group bounds, GEMM row tiles */
+    MOE_K_SCATTER = 2,        /* row table */
+    MOE_K_GEMM_GATE_UP = 3,   /* GU grouped GEMM */
+    MOE_K_SWIGLU_Q8 = 4,      /* H = SwiGLU(GU), Hq = Q8(H) */
+    MOE_K_GEMM_DOWN = 5,      /* Dm grouped GEMM */
+    MOE_K_COMBINE = 6         /* y = weighted combine */
 };
 
 typedef struct moe_kernel_times {

@@ -17,6 +17,7 @@ struct GemmArgs {
     const int32_t* ntiles;    // number of valid tiles (device)
     float* out;               // [R, N]
     int N, K;
+    int E;                    // experts in the blob (tile expert indices are clamped to it)
     int gu_f;                 // f of the interleaved gate/up matrix (gate/up launch only)
 };
 
@@ -38,6 +39,7 @@ struct LayerLaunch {
     int32_t* rows;
     int32_t* pos;
     int32_t* rtok;
+    uint32_t* done;           // grouping hand-off counter (zero between layers)
     int8_t* xq;
     float* dx;
     float* gu;
@@ -50,10 +52,10 @@ struct LayerLaunch {
 };
 
 // kernel ids in launch order (timing)
-enum KernelId { kRoute, kQuantX, kGroupPrefix, kGroupBounds, kScatter, kGemmGateUp, kSwigluQ8,
-                kGemmDown, kCombine, kNumKernels };
+enum KernelId { kRouteQuant, kGroup, kScatter, kGemmGateUp, kSwigluQ8, kGemmDown, kCombine,
+                kNumKernels };
 
-// route, quantise X, group, scatter, GU GEMM, SwiGLU+Q8, down GEMM (last reader
+// route + quantise X, group (bounds, tiles, row table), GU GEMM, SwiGLU+Q8, down GEMM (last reader
 // of the weights) -- everything up to the combine.
 hipError_t launch_layer(const LayerLaunch& L, hipStream_t st);
 // combine (and clear the membership mask for the next layer)

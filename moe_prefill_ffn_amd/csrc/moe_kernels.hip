@@ -92,89 +92,89 @@ __device__ __forceinline__ uint32_t q8_block_of8(float4 v, float* scale)
     return pack4(q8_code(v.x, d), q8_code(v.y, d), q8_code(v.z, d), q8_code(v.w, d));
 }
 
-// ---------------------------------------------------------------- route ---
-// One wave per token.  Lane l holds logits l, l+64, ...  Each of the k rounds
-// takes the best remaining (logit, index) pair -- larger logit, then lower
-// index -- by a butterfly over the wave.  Also sets the token's bit in the
-// expert membership mask used by the grouping step.
-__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E,
-                                               int k, int32_t* __restrict__ eidx,
-                                               float* __restrict__ wts, uint32_t* __restrict__ mask,
-                                               int W)
+// ------------------------------------------------------- route + quantise ---
+// One launch, two kinds of workgroup.  Workgroups [0, n_route) route 4 tokens
+// each (one wave per token); the rest quantise X to Q8.
+//
+// Routing: the rank of logit e among the token's E logits is the number of
+// logits that beat it -- larger value, or equal value and lower index.  With
+// key(e) = (order-preserving bits of the logit, with -0 read as +0) << 32 |
+// (2^32 - 1 - e), "beats" is one unsigned 64-bit compare, so every lane ranks
+// its own logits against all E keys broadcast from LDS.  The logit of rank
+// j < k is slot j.  Router weights: softmax over the k selected logits, summed
+// in ascending slot order.  Each selected (token, expert) also sets the token's
+// bit in the expert membership mask read by the grouping step.
+constexpr int kRouteMaxE = 1024;
+
+__device__ __forceinline__ uint64_t route_key(float v, int e)
 {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const int nper = (E + 63) >> 6;   // <= 16
-    float v[16];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int e = lane + 64 * i;
-        if (i < nper && e < E) {
-            v[i] = logits[(int64_t)t * E + e];
-        } else {
-            v[i] = 0.0f;
-            taken |= 1u << i;
-        }
-    }
-    float my_v = 0.0f;
-    int my_i = 0;
-    for (int j = 0; j < k; ++j) {
-        float bv = -__int_as_float(0x7f800000);
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (i < nper && !((taken >> i) & 1u)) {
-                const int e = lane + 64 * i;
-                if (v[i] > bv || (v[i] == bv && e < bi)) {
-                    bv = v[i];
-                    bi = e;
-                }
-            }
-        }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            const float ov = __shfl_xor(bv, m);
-            const int oi = __shfl_xor(bi, m);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-        if (lane == j) {
-            my_v = bv;
-            my_i = bi;
-        }
-    }
-    // softmax over the k selected logits; sum in ascending slot order
-    const float top = __shfl(my_v, 0);
-    const float z = lane < k ? exp_cw(my_v - top) : 0.0f;
-    float s = 0.0f;
-    for (int j = 0; j < k; ++j) s += __shfl(z, j);
-    if (lane < k) {
-        eidx[(int64_t)t * k + lane] = my_i;
-        wts[(int64_t)t * k + lane] = z / s;
-        atomicOr(&mask[(int64_t)my_i * W + (t >> 5)], 1u << (t & 31));
-    }
+    uint32_t u = v == 0.0f ? 0u : __float_as_uint(v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
-// ------------------------------------------------------------- quantise ---
-// x is a flat array of n_blocks 32-float blocks (a row-major [rows, K] matrix
-// with K % 32 == 0).  8 lanes per block, 4 values per lane.
-__global__ __launch_bounds__(256) void k_quant_q8(const float* __restrict__ x, int64_t n_blocks,
-                                                  int8_t* __restrict__ q, float* __restrict__ scale)
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
+                                            int32_t* __restrict__ eidx, float* __restrict__ wts,
+                                            uint32_t* __restrict__ mask, int W, uint64_t* keys,
+                                            float* zsel)
 {
-    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t blk = g >> 3;
-    if (blk >= n_blocks) return;          // whole 8-lane groups exit together
+    const int lane = threadIdx.x & 63;
+    const float* lt = logits + (int64_t)t * E;
+    for (int e = lane; e < E; e += 64) keys[e] = route_key(lt[e], e);
+    __builtin_amdgcn_wave_barrier();
+    for (int e = lane; e < E; e += 64) {
+        const uint64_t me = keys[e];
+        int rank = 0;
+        for (int c = 0; c < E; ++c) rank += keys[c] > me ? 1 : 0;
+        if (rank < k) {
+            eidx[(int64_t)t * k + rank] = e;
+            zsel[rank] = lt[e];
+            atomicOr(&mask[(int64_t)e * W + (t >> 5)], 1u << (t & 31));
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const float top = zsel[0];
+    const float z = lane < k ? exp_cw(zsel[lane] - top) : 0.0f;
+    __builtin_amdgcn_wave_barrier();
+    if (lane < k) zsel[lane] = z;
+    __builtin_amdgcn_wave_barrier();
+    float sum = 0.0f;
+    for (int j = 0; j < k; ++j) sum += zsel[j];
+    if (lane < k) wts[(int64_t)t * k + lane] = z / sum;
+}
+
+// x is a flat array of n_blocks 32-float blocks (a row-major [rows, K] matrix
+// with K % 32 == 0); 8 lanes per block, 4 values per lane.
+__device__ __forceinline__ void quant_block8(const float* __restrict__ x, int64_t blk,
+                                             int8_t* __restrict__ q, float* __restrict__ scale)
+{
     const int sub = threadIdx.x & 7;
     const float4 v = *reinterpret_cast<const float4*>(x + blk * 32 + sub * 4);
     float d;
     const uint32_t packed = q8_block_of8(v, &d);
     *reinterpret_cast<uint32_t*>(q + blk * 32 + sub * 4) = packed;
     if (sub == 0) scale[blk] = d;
+}
+
+__global__ __launch_bounds__(256) void k_route_quant(const float* __restrict__ logits, int T, int E,
+                                                     int k, int32_t* __restrict__ eidx,
+                                                     float* __restrict__ wts,
+                                                     uint32_t* __restrict__ mask, int W,
+                                                     int n_route, const float* __restrict__ x,
+                                                     int64_t n_blocks, int8_t* __restrict__ xq,
+                                                     float* __restrict__ dx)
+{
+    __shared__ uint64_t keys[4][kRouteMaxE];
+    __shared__ float zsel[4][64];
+    if ((int)blockIdx.x < n_route) {
+        const int wave = threadIdx.x >> 6;
+        const int t = blockIdx.x * 4 + wave;
+        if (t < T) route_token(logits, t, E, k, eidx, wts, mask, W, keys[wave], zsel[wave]);
+        return;
+    }
+    const int64_t g = (int64_t)(blockIdx.x - n_route) * 256 + threadIdx.x;
+    const int64_t blk = g >> 3;
+    if (blk < n_blocks) quant_block8(x, blk, xq, dx);   // whole 8-lane groups together
 }
 
 // ---------------------------------------------------------- SwiGLU + Q8 ---
@@ -206,18 +206,33 @@ __global__ __launch_bounds__(256) void k_swiglu_q8(const float* __restrict__ gu,
 }
 
 // ---------------------------------------------------------------- group ---
-// Per expert: exclusive prefix of the membership-mask popcounts over the
-// 32-token words, and the expert's row count.
-__global__ __launch_bounds__(256) void k_group_prefix(const uint32_t* __restrict__ mask, int W,
-                                                      int32_t* __restrict__ wprefix,
-                                                      int32_t* __restrict__ counts)
+// The row table is a stable counting sort of the pairs p = t*k + j on their
+// expert.  Word w of expert e in the membership mask holds tokens 32w..32w+31
+// routed to e.
+//
+// k_group: one workgroup per expert computes the exclusive prefix of the word
+// popcounts and the expert's row count.  The last workgroup to finish (a
+// device-scope counter, release/acquire fences around it) then computes the
+// group bounds (exclusive scan of the counts) and the GEMM row-tile list
+// (expert, first row, end row; kBM rows per tile; expert order), and resets the
+// counter for the next layer.
+constexpr int kGroupThreads = 256;
+
+__global__ __launch_bounds__(kGroupThreads) void k_group(const uint32_t* __restrict__ mask, int W,
+                                                         int E, int32_t* __restrict__ wprefix,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ bounds,
+                                                         int32_t* __restrict__ tiles,
+                                                         int32_t* __restrict__ ntiles,
+                                                         uint32_t* __restrict__ done)
 {
-    __shared__ int wave_tot[4];
+    __shared__ int s_tot[4];
+    __shared__ int s_last;
     const int e = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int running = 0;
-    for (int base = 0; base < W; base += 256) {
-        const int w = base + threadIdx.x;
+    for (int base = 0; base < W; base += kGroupThreads) {
+        const int w = base + tid;
         const int c = w < W ? __popc(mask[(int64_t)e * W + w]) : 0;
         int incl = c;
 #pragma unroll
@@ -225,34 +240,38 @@ __global__ __launch_bounds__(256) void k_group_prefix(const uint32_t* __restrict
             const int y = __shfl_up(incl, o);
             if (lane >= o) incl += y;
         }
-        if (lane == 63) wave_tot[wave] = incl;
+        if (lane == 63) s_tot[wave] = incl;
         __syncthreads();
         int before = 0, total = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            before += i < wave ? wave_tot[i] : 0;
-            total += wave_tot[i];
+            before += i < wave ? s_tot[i] : 0;
+            total += s_tot[i];
         }
         if (w < W) wprefix[(int64_t)e * W + w] = running + before + incl - c;
         running += total;
         __syncthreads();
     }
-    if (threadIdx.x == 0) counts[e] = running;
-}
+    if (tid == 0) {
+        counts[e] = running;
+        __threadfence();                                  // publish counts[e] device-wide
+        s_last = atomicAdd(done, 1u) == (uint32_t)(E - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();                                      // see every workgroup's counts
 
-// One workgroup: group bounds (exclusive scan of counts) and the GEMM row-tile
-// list (expert, first row, end row) in expert order, kBM rows per tile.
-__global__ __launch_bounds__(1024) void k_group_bounds(const int32_t* __restrict__ counts, int E,
-                                                       int32_t* __restrict__ bounds,
-                                                       int32_t* __restrict__ tiles,
-                                                       int32_t* __restrict__ ntiles)
-{
-    __shared__ int tot_c[16], tot_t[16];
-    const int e = threadIdx.x;
-    const int lane = e & 63, wave = e >> 6;
-    const int c = e < E ? counts[e] : 0;
-    const int nt = (c + kBM - 1) / kBM;
-    int ic = c, it = nt;
+    // last workgroup: bounds and tiles, 4 experts per thread (E <= 1024)
+    int c4[4], t4[4], sc = 0, st = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ee = tid * 4 + i;
+        c4[i] = ee < E ? __hip_atomic_load(&counts[ee], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        t4[i] = (c4[i] + kBM - 1) / kBM;
+        sc += c4[i];
+        st += t4[i];
+    }
+    int ic = sc, it = st;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const int yc = __shfl_up(ic, o);
@@ -262,38 +281,46 @@ __global__ __launch_bounds__(1024) void k_group_bounds(const int32_t* __restrict
             it += yt;
         }
     }
+    __shared__ int s_wc[4], s_wt[4];
     if (lane == 63) {
-        tot_c[wave] = ic;
-        tot_t[wave] = it;
+        s_wc[wave] = ic;
+        s_wt[wave] = it;
     }
     __syncthreads();
     int bc = 0, bt = 0, all_c = 0, all_t = 0;
-    for (int i = 0; i < 16; ++i) {
-        bc += i < wave ? tot_c[i] : 0;
-        bt += i < wave ? tot_t[i] : 0;
-        all_c += tot_c[i];
-        all_t += tot_t[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bc += i < wave ? s_wc[i] : 0;
+        bt += i < wave ? s_wt[i] : 0;
+        all_c += s_wc[i];
+        all_t += s_wt[i];
     }
-    if (e < E) {
-        const int start = bc + ic - c;
-        const int tstart = bt + it - nt;
-        bounds[e] = start;
-        for (int i = 0; i < nt; ++i) {
-            const int r0 = start + i * kBM;
-            const int r1 = r0 + kBM < start + c ? r0 + kBM : start + c;
-            tiles[3 * (tstart + i) + 0] = e;
-            tiles[3 * (tstart + i) + 1] = r0;
-            tiles[3 * (tstart + i) + 2] = r1;
+    int start = bc + ic - sc, tstart = bt + it - st;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ee = tid * 4 + i;
+        if (ee < E) {
+            bounds[ee] = start;
+            for (int q = 0; q < t4[i]; ++q) {
+                const int r0 = start + q * kBM;
+                const int r1 = r0 + kBM < start + c4[i] ? r0 + kBM : start + c4[i];
+                tiles[3 * (tstart + q) + 0] = ee;
+                tiles[3 * (tstart + q) + 1] = r0;
+                tiles[3 * (tstart + q) + 2] = r1;
+            }
         }
+        start += c4[i];
+        tstart += t4[i];
     }
-    if (e == 0) {
+    if (tid == 0) {
         bounds[E] = all_c;
         *ntiles = all_t;
+        *done = 0u;                                       // ready for the next layer
     }
 }
 
-// Row table: pair p = t*k + j goes to row bounds[e] + (number of tokens
-// before t routed to e), read off the membership mask -- a stable order in p.
+// Row table: pair p = t*k + j goes to row bounds[e] + prefix[e][t/32] + (tokens
+// of word t/32 before t routed to e) -- stable in p.
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eidx, int64_t R, int k,
                                                  const uint32_t* __restrict__ mask,
                                                  const int32_t* __restrict__ wprefix,
@@ -395,7 +422,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
     const int tau = xcd < r8 ? xcd * (q8 + 1) + slot : r8 * (q8 + 1) + (xcd - r8) * q8 + slot;
     const int tile = tau / NG, ng = tau - tile * NG;
 
-    const int e = g.tiles[3 * tile + 0];
+    const int te = g.tiles[3 * tile + 0];
+    const int e = te < 0 ? 0 : (te >= g.E ? g.E - 1 : te); // always valid; a no-op for a sound list
     const int r0 = g.tiles[3 * tile + 1];
     const int nrows = g.tiles[3 * tile + 2] - r0;          // 1 .. kBM
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -582,20 +610,16 @@ static inline void mark(const LayerLaunch& L, int i, hipStream_t st)
 hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
 {
     const int64_t R = (int64_t)L.T * L.k;
-    mark(L, 0, st);
-    hipLaunchKernelGGL(k_route, dim3(nblk(L.T, 4)), dim3(256), 0, st, L.logits, L.T, L.E, L.k,
-                       L.eidx, L.wts, L.mask, L.W);
+    const int n_route = (int)nblk(L.T, 4);
     const int64_t xblocks = (int64_t)L.T * (L.d / 32);
-    mark(L, 1, st);
-    hipLaunchKernelGGL(k_quant_q8, dim3(nblk(xblocks * 8, 256)), dim3(256), 0, st, L.x, xblocks,
+    mark(L, kRouteQuant, st);
+    hipLaunchKernelGGL(k_route_quant, dim3(n_route + nblk(xblocks * 8, 256)), dim3(256), 0, st,
+                       L.logits, L.T, L.E, L.k, L.eidx, L.wts, L.mask, L.W, n_route, L.x, xblocks,
                        L.xq, L.dx);
-    mark(L, 2, st);
-    hipLaunchKernelGGL(k_group_prefix, dim3(L.E), dim3(256), 0, st, L.mask, L.W, L.wprefix,
-                       L.counts);
-    mark(L, 3, st);
-    hipLaunchKernelGGL(k_group_bounds, dim3(1), dim3(1024), 0, st, L.counts, L.E, L.bounds, L.tiles,
-                       L.ntiles);
-    mark(L, 4, st);
+    mark(L, kGroup, st);
+    hipLaunchKernelGGL(k_group, dim3(L.E), dim3(kGroupThreads), 0, st, L.mask, L.W, L.E, L.wprefix,
+                       L.counts, L.bounds, L.tiles, L.ntiles, L.done);
+    mark(L, kScatter, st);
     hipLaunchKernelGGL(k_scatter, dim3(nblk(R, 256)), dim3(256), 0, st, L.eidx, R, L.k, L.mask,
                        L.wprefix, L.bounds, L.W, L.rows, L.pos, L.rtok);
     const int max_tiles_now = (int)((R + kBM - 1) / kBM) + (L.E < R ? L.E : (int)R);
@@ -613,12 +637,13 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     gu.out = L.gu;
     gu.N = 2 * L.f;
     gu.K = L.d;
+    gu.E = L.E;
     gu.gu_f = L.f;
-    mark(L, 5, st);
+    mark(L, kGemmGateUp, st);
     hipLaunchKernelGGL(k_gemm_gate_up, dim3(nblk(gu.N / 32, 4) * max_tiles_now), dim3(256), 0, st, gu);
 
     const int64_t hblocks = R * (L.f / 32);
-    mark(L, 6, st);
+    mark(L, kSwigluQ8, st);
     hipLaunchKernelGGL(k_swiglu_q8, dim3(nblk(hblocks * 8, 256)), dim3(256), 0, st, L.gu, R, L.f,
                        L.hq, L.dh, L.h_out);
 
@@ -632,9 +657,9 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     dn.N = L.d;
     dn.K = L.f;
     dn.gu_f = 0;
-    mark(L, 7, st);
+    mark(L, kGemmDown, st);
     hipLaunchKernelGGL(k_gemm_down, dim3(nblk(dn.N / 32, 4) * max_tiles_now), dim3(256), 0, st, dn);
-    mark(L, 8, st);
+    mark(L, kCombine, st);
     return hipGetLastError();
 }
 
@@ -644,7 +669,7 @@ hipError_t launch_combine(const LayerLaunch& L, hipStream_t st)
     const int64_t mw = (int64_t)L.E * L.W;
     hipLaunchKernelGGL(k_combine, dim3(nblk(work > mw ? work : mw, 256)), dim3(256), 0, st, L.dm,
                        L.wts, L.pos, L.T, L.k, L.d, L.y, L.mask, mw);
-    mark(L, 9, st);
+    mark(L, kNumKernels, st);
     return hipGetLastError();
 }
 

@@ -363,6 +363,7 @@ int moe_prefill_create(const moe_prefill_params_t* pin, moe_prefill_t** out)
     }
     e = hipStreamCreateWithFlags(&h->copy, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipMemset(h->ws + h->L.mask, 0, (size_t)h->E * h->L.W * 4);
+    if (e == hipSuccess) e = hipMemset(h->ws + h->L.done, 0, 4);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         const int rc = hip_fail(nullptr, e, "create");
@@ -436,9 +437,10 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
         blob = h->pool + (uint64_t)slot * h->slot_bytes;
     }
 
-    if (h->mask_dirty) {
+    if (h->mask_dirty) {   // a launch failed part-way: restore the grouping state first
         e = launch_fill_u32(reinterpret_cast<uint32_t*>(h->ws + h->L.mask), (int64_t)h->E * h->L.W, 0u, st);
-        if (e != hipSuccess) return hip_fail(h, e, "mask clear");
+        if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(h->ws + h->L.done), 1, 0u, st);
+        if (e != hipSuccess) return hip_fail(h, e, "grouping state reset");
         h->mask_dirty = false;
     }
 
@@ -470,6 +472,7 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
     LL.rows = reinterpret_cast<int32_t*>(w + h->L.rows);
     LL.pos = reinterpret_cast<int32_t*>(w + h->L.pos);
     LL.rtok = reinterpret_cast<int32_t*>(w + h->L.rtok);
+    LL.done = reinterpret_cast<uint32_t*>(w + h->L.done);
     LL.xq = reinterpret_cast<int8_t*>(w + h->L.xq);
     LL.dx = reinterpret_cast<float*>(w + h->L.dx);
     LL.gu = reinterpret_cast<float*>(w + h->L.gu);
@@ -718,8 +721,7 @@ int moe_prefill_set_timing(moe_prefill_t* h, int32_t enable)
 
 const char* moe_prefill_kernel_name(int32_t id)
 {
-    static const char* names[kNumKernels] = {"route_topk", "quant_x_q8", "group_prefix",
-                                             "group_bounds", "row_scatter", "gemm_gate_up",
+    static const char* names[kNumKernels] = {"route_quant", "group", "row_scatter", "gemm_gate_up",
                                              "swiglu_q8", "gemm_down", "combine"};
     return (id >= 0 && id < kNumKernels) ? names[id] : "";
 }
