@@ -8,7 +8,7 @@ namespace moe {
 
 struct GemmArgs {
     const int8_t* A;          // activation codes [rows, K]
-    const float* A_scale;     // their block scales [rows, K/32]
+    const float* A_scale;     // their block scales [rows][a_scale_stride], blocks 0 .. K/32-1 used
     const int32_t* row_src;   // grouped row -> A row (gate/up launch; the down launch reads row r)
     const uint8_t* blob;      // layer weight blob
     uint64_t expert_stride;   // bytes per expert
@@ -19,6 +19,7 @@ struct GemmArgs {
     int N, K;
     int E;                    // experts in the blob (tile expert indices are clamped to it)
     int gu_f;                 // f of the interleaved gate/up matrix (gate/up launch only)
+    int a_scale_stride;       // floats per A_scale row (a multiple of the 8-block scale group)
 };
 
 struct LayerLaunch {

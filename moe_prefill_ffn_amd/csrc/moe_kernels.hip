@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe_layout.h"
 #include "moe_kernels.h"
 
@@ -145,15 +147,20 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
 
 // x is a flat array of n_blocks 32-float blocks (a row-major [rows, K] matrix
 // with K % 32 == 0); 8 lanes per block, 4 values per lane.
-__device__ __forceinline__ void quant_block8(const float* __restrict__ x, int64_t blk,
-                                             int8_t* __restrict__ q, float* __restrict__ scale)
+// block blk = row * nbk + b; its scale goes to scale[row * stride + b]
+__device__ __forceinline__ void quant_block8(const float* __restrict__ x, int64_t blk, int nbk,
+                                             int stride, int8_t* __restrict__ q,
+                                             float* __restrict__ scale)
 {
     const int sub = threadIdx.x & 7;
     const float4 v = *reinterpret_cast<const float4*>(x + blk * 32 + sub * 4);
     float d;
     const uint32_t packed = q8_block_of8(v, &d);
     *reinterpret_cast<uint32_t*>(q + blk * 32 + sub * 4) = packed;
-    if (sub == 0) scale[blk] = d;
+    if (sub == 0) {
+        const int64_t row = blk / nbk;
+        scale[row * stride + (blk - row * nbk)] = d;
+    }
 }
 
 __global__ __launch_bounds__(256) void k_route_quant(const float* __restrict__ logits, int T, int E,
@@ -161,8 +168,8 @@ __global__ __launch_bounds__(256) void k_route_quant(const float* __restrict__ l
                                                      float* __restrict__ wts,
                                                      uint32_t* __restrict__ mask, int W,
                                                      int n_route, const float* __restrict__ x,
-                                                     int64_t n_blocks, int8_t* __restrict__ xq,
-                                                     float* __restrict__ dx)
+                                                     int64_t n_blocks, int nbk, int dx_stride,
+                                                     int8_t* __restrict__ xq, float* __restrict__ dx)
 {
     __shared__ uint64_t keys[4][kRouteMaxE];
     __shared__ float zsel[4][64];
@@ -174,14 +181,14 @@ __global__ __launch_bounds__(256) void k_route_quant(const float* __restrict__ l
     }
     const int64_t g = (int64_t)(blockIdx.x - n_route) * 256 + threadIdx.x;
     const int64_t blk = g >> 3;
-    if (blk < n_blocks) quant_block8(x, blk, xq, dx);   // whole 8-lane groups together
+    if (blk < n_blocks) quant_block8(x, blk, nbk, dx_stride, xq, dx);   // whole 8-lane groups together
 }
 
 // ---------------------------------------------------------- SwiGLU + Q8 ---
 // gu [R, 2f] (gate | up) -> h = silu(gate) * up -> Q8 blocks of 32 along f.
 __global__ __launch_bounds__(256) void k_swiglu_q8(const float* __restrict__ gu, int64_t R, int f,
                                                    int8_t* __restrict__ hq, float* __restrict__ dh,
-                                                   float* __restrict__ h_out)
+                                                   int dh_stride, float* __restrict__ h_out)
 {
     const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int nbf = f >> 5;
@@ -202,7 +209,7 @@ __global__ __launch_bounds__(256) void k_swiglu_q8(const float* __restrict__ gu,
     float d;
     const uint32_t packed = q8_block_of8(hv, &d);
     *reinterpret_cast<uint32_t*>(hq + r * f + b * 32 + sub * 4) = packed;
-    if (sub == 0) dh[blk] = d;
+    if (sub == 0) dh[r * dh_stride + b] = d;
 }
 
 // ---------------------------------------------------------------- group ---
@@ -353,41 +360,43 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
 //
 // K advances one packed pair (2 blocks, 64 K) per stage through a 4-deep LDS
 // ring filled by direct global->LDS loads (no register staging), issued three
-// stages ahead.  Per stage and wave exactly three loads: 1 KiB of gathered A
-// rows, the wave's 1 KiB of packed Q4 weights, and 256 B holding the wave's
-// fp16 weight scales (lanes 0-31) and the A block scales of 16 rows (lanes
-// 32-63).  A is stored as 128-byte "super-rows" (two 64-byte rows) whose
-// 16-byte chunks are XOR-swizzled by the super-row index, which makes the MFMA
-// operand reads bank-conflict free.
+// stages ahead: per stage and wave 1 KiB of gathered A rows and the wave's
+// 1 KiB of packed Q4 weights.  A is stored as 128-byte "super-rows" (two
+// 64-byte rows) whose 16-byte chunks are XOR-swizzled by the super-row index,
+// which makes the MFMA operand reads bank-conflict free.  The block scales
+// come in groups of 8 blocks (4 stages) into a double-buffered LDS area, one
+// 16-byte load per lane: lanes 0-31 the fp16 scales of the wave's 32 weight
+// columns, lanes 32-63 the fp32 A scales of 16 rows (two lanes per row).
 //
-// Per 32-block the matrix cores do all products: two v_mfma_i32_32x32x32_i8
-// give the exact int32 block sums of both row halves, and one
-// v_mfma_f32_32x32x1_2b_f32 gives the rank-1 scale products
-// a_scale[row] * w_scale[col] of both halves (one rounding each, as a plain
-// fp32 multiply).  The VALU is left with convert + fma per element.
+// Per 32-block the matrix cores do all products: one v_mfma_f32_32x32x1_2b_f32
+// gives the scale products a_scale[row] * w_scale[col] of both row halves (one
+// rounding each, as a plain fp32 multiply), and per row half one
+// v_mfma_i32_32x32x32_i8 gives the exact int32 block sums.  The VALU is left
+// with unpacking the nibbles and the convert + fma per element.  The row halves
+// are processed one after the other, which keeps a wave under 128 VGPRs (four
+// waves per SIMD).
 //
 // Workgroups are numbered so that each XCD (dispatch is round-robin over the
 // 8 XCDs) receives a contiguous run of tiles: the n-groups of a row tile and
 // the row tiles of an expert share that XCD's L2.
-constexpr int kRing = 4;                  // LDS stages in flight
+constexpr int kRing = 4;                  // LDS stages = stages per scale group
 constexpr int kA_OFF = 0;                 // [32 super-rows][8 chunks of 16 B], swizzled
 constexpr int kB_OFF = 4096;              // [4 waves][64 lanes][16 B]
-constexpr int kSX_OFF = 8192;             // [4 waves][ {32 cols x 2 fp16} | {16 rows x 2 fp32} ]
-constexpr int kStageBytes = 9216;
+constexpr int kStageBytes = 8192;
+constexpr int kScaleBytes = 4096;         // [4 waves][ {32 cols x 8 fp16} | {16 rows x 8 fp32} ]
+static_assert(kRing * 2 == kScaleGroup, "one scale group per pass over the ring");
 
 typedef float v32f __attribute__((ext_vector_type(32)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 __device__ __forceinline__ uint32_t nib_to_i8(uint32_t v)   // 4 offset-binary nibbles -> 4 int8
 {
     return (v + 0x78787878u) ^ 0x80808080u;
 }
 
-// Direct global->LDS loads: lane i's 16 (or 4) bytes from g land at LDS
-// wave_base + 16 i (4 i).  Issued as inline asm so the compiler's wait-count
-// bookkeeping does not track them: the ring below waits for them explicitly
-// (vmcnt) and never lets the compiler drain loads still meant to be in flight.
+// Direct global->LDS loads: lane i's 16 bytes from g land at LDS wave_base + 16 i.
+// Issued as inline asm so the compiler's wait-count bookkeeping does not track
+// them: the ring below waits for them explicitly (vmcnt) and never lets the
+// compiler drain loads still meant to be in flight.
 __device__ __forceinline__ uint32_t lds_addr(const void* p)
 {
     return __builtin_amdgcn_readfirstlane(
@@ -396,11 +405,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
 __device__ __forceinline__ void g2lds16(const void* g, const uint8_t* wave_base)
 {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds_addr(wave_base)) : "memory", "m0");
-}
-__device__ __forceinline__ void g2lds4(const void* g, const uint8_t* wave_base)
-{
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                  :: "v"(g), "s"(lds_addr(wave_base)) : "memory", "m0");
 }
 
@@ -428,16 +432,13 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
     const int nrows = g.tiles[3 * tile + 2] - r0;          // 1 .. kBM
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = g.K, N = g.N;
-    const int nbk = K >> 5, npairs = K >> 6;
+    const int npairs = K >> 6, ngroups = scale_groups(K);
     const int nt_real = ng * 4 + wave;
     const bool wave_on = nt_real < (N >> 5);
     const int nt = wave_on ? nt_real : (N >> 5) - 1;      // idle waves load valid memory
 
-    // ring of four LDS stage slots (the loop below is unrolled over the slots)
-    __shared__ __attribute__((aligned(16))) uint8_t ring0[kStageBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t ring1[kStageBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t ring2[kStageBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t ring3[kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t sbuf[2 * kScaleBytes];
 
     // ---- load sources (all addresses clamped in bounds)
     // A: this wave fills super-rows 8w..8w+7, lane -> super-row 8w + lane/8, slot lane%8
@@ -452,29 +453,34 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
         a_src = g.A + (int64_t)src * K;
         a_col = (cis & 3) * 16;
     }
-    // scales: lanes 0-31 -> fp16 pair scales of weight column lane, lanes 32-63 -> A block
-    // scales of row 16w + (lane-32)/2, block (lane & 1) of the pair
     const uint8_t* ex = g.blob + (uint64_t)e * g.expert_stride;
     const uint8_t* wq = ex + g.q_off + (uint64_t)nt * npairs * 1024 + lane * 16;
-    const uint8_t* sx_src;
-    int sx_step;
+    // scale groups: lanes 0-31 -> fp16 scales of weight column lane (16 B per group),
+    // lanes 32-63 -> A scales of row 16w + (lane-32)/2, blocks 4*((lane-32)&1) .. +3
+    const uint8_t* sc_src;
+    int sc_step;
     if (lane < 32) {
-        sx_src = ex + g.s_off + (uint64_t)nt * npairs * 128 + lane * 4;
-        sx_step = 128;
+        sc_src = ex + g.s_off + ((uint64_t)nt * ngroups * 32 + lane) * 16;
+        sc_step = 32 * 16;
     } else {
         const int row = 16 * wave + ((lane - 32) >> 1);
         const int rr = r0 + (row < nrows ? row : nrows - 1);
         const int src = kGateUp ? g.row_src[rr] : rr;
-        sx_src = reinterpret_cast<const uint8_t*>(g.A_scale + (int64_t)src * nbk + (lane & 1));
-        sx_step = 8;
+        sc_src = reinterpret_cast<const uint8_t*>(g.A_scale + (int64_t)src * g.a_scale_stride +
+                                                  ((lane - 32) & 1) * 4);
+        sc_step = kScaleGroup * 4;
     }
 
-    // stage = packed pair pr (clamped: tail stages reload the last pair, never read)
-    auto issue = [&](int pr, uint8_t* sb) {
+    // stage = packed pair pr, scale group grp (clamped: tail loads repeat the
+    // last one, never read)
+    auto issue_stage = [&](int pr, uint8_t* sb) {
         const int p = pr < npairs ? pr : npairs - 1;
         g2lds16(a_src + p * 64 + a_col, sb + kA_OFF + wave * 1024);
         g2lds16(wq + (uint64_t)p * 1024, sb + kB_OFF + wave * 1024);
-        g2lds4(sx_src + (uint64_t)p * sx_step, sb + kSX_OFF + wave * 256);
+    };
+    auto issue_scales = [&](int grp, uint8_t* sc) {
+        const int gg = grp < ngroups ? grp : ngroups - 1;
+        g2lds16(sc_src + (int64_t)gg * sc_step, sc + wave * 1024);
     };
 
     float acc0[16], acc1[16];
@@ -483,7 +489,6 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
         acc0[i] = 0.0f;
         acc1[i] = 0.0f;
     }
-    const bool two = nrows > 32;
     const int h = lane >> 5, j32 = lane & 31;
     const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     v32f fzero;
@@ -492,20 +497,30 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
     // A-operand offsets (chunk index depends on the block of the pair: 2*q + h)
     const int a_off0[2] = {a_lds_off(j32, h), a_lds_off(j32, 2 + h)};
     const int a_off1[2] = {a_lds_off(32 + j32, h), a_lds_off(32 + j32, 2 + h)};
-    // this lane's A scales (row = lane) live in wave (lane/16)'s scale region
-    const int x_off = kSX_OFF + (lane >> 4) * 256 + 128 + (lane & 15) * 8;
+    // scale-area offsets: this lane's column scales, and the A scales of row = lane
+    const int ws_off = wave * 1024 + j32 * 16;
+    const int xs_off = (lane >> 4) * 1024 + 512 + (lane & 15) * 32;
 
-    // one stage: wait for its loads, sync, queue the stage three ahead into the
-    // slot freed by the previous stage, then two blocks of MFMA + epilogue
-    auto stage = [&](int s, const uint8_t* sb, uint8_t* sb_next3) {
-        // this wave's stage-s loads have landed (stages s+1, s+2 may still fly), then
-        // everyone's have, and stage s-1 is fully read so its slot can be refilled
-        asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
-        issue(s + kRing - 1, sb_next3);
+    // one stage (U = position in the scale group): wait for its loads, sync,
+    // queue the stage three ahead into the slot freed by the previous stage
+    // (and, at a group start, the next group's scales), then two blocks of
+    // MFMA + epilogue
+    auto stage = [&](auto two_c, auto u_c, int s) {
+        constexpr bool kTwo = decltype(two_c)::value;
+        constexpr int U = decltype(u_c)::value;
+        // loads issued after this stage's: two per later stage in flight, plus the
+        // scale load issued at the start of a group if that came after them
+        constexpr int kLater = 2 * (kRing - 2) + ((U == 1 || U == 2) ? 1 : 0);
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(kLater) : "memory");
+        const int grp = s >> 2;
+        if (U == 0) issue_scales(grp + 1, sbuf + ((grp + 1) & 1) * kScaleBytes);
+        issue_stage(s + kRing - 1, ring + ((U + kRing - 1) % kRing) * kStageBytes);
         if (!wave_on) return;
+        const uint8_t* sb = ring + U * kStageBytes;
+        const uint8_t* sc = sbuf + (grp & 1) * kScaleBytes;
         const uint4 bq = *reinterpret_cast<const uint4*>(sb + kB_OFF + wave * 1024 + lane * 16);
-        const uint32_t bs = *reinterpret_cast<const uint32_t*>(sb + kSX_OFF + wave * 256 + j32 * 4);
-        const float2 dx = *reinterpret_cast<const float2*>(sb + x_off);
+        const uint32_t bs = *reinterpret_cast<const uint32_t*>(sc + ws_off + U * 4);
+        const float2 dx = *reinterpret_cast<const float2*>(sc + xs_off + (U >> 1) * 16 + (U & 1) * 8);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const uint32_t w0 = q ? bq.z : bq.x;
@@ -525,24 +540,31 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc0[i] = __builtin_fmaf((float)is[i], t[i], acc0[i]);
             }
-            if (two) {
+            __builtin_amdgcn_sched_barrier(0);   // keep the halves apart: low register pressure
+            if (kTwo) {
                 const v4i a = *reinterpret_cast<const v4i*>(sb + kA_OFF + a_off1[q]);
                 const v16i is = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop, zero, 0, 0, 0);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc1[i] = __builtin_fmaf((float)is[i], t[16 + i], acc1[i]);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
-
-    issue(0, ring0);
-    issue(1, ring1);
-    issue(2, ring2);
-    for (int s = 0; s < npairs; s += kRing) {
-        stage(s, ring0, ring3);
-        if (s + 1 < npairs) stage(s + 1, ring1, ring0);
-        if (s + 2 < npairs) stage(s + 2, ring2, ring1);
-        if (s + 3 < npairs) stage(s + 3, ring3, ring2);
-    }
+    auto run = [&](auto two_c) {
+        issue_scales(0, sbuf);
+#pragma unroll
+        for (int u = 0; u < kRing - 1; ++u) issue_stage(u, ring + u * kStageBytes);
+        for (int s0 = 0; s0 < npairs; s0 += kRing) {
+            stage(two_c, std::integral_constant<int, 0>{}, s0);
+            if (s0 + 1 < npairs) stage(two_c, std::integral_constant<int, 1>{}, s0 + 1);
+            if (s0 + 2 < npairs) stage(two_c, std::integral_constant<int, 2>{}, s0 + 2);
+            if (s0 + 3 < npairs) stage(two_c, std::integral_constant<int, 3>{}, s0 + 3);
+        }
+    };
+    if (nrows > 32)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped tail loads before exit
 
     if (!wave_on) return;
@@ -560,9 +582,9 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
 
 // gate/up projection: A rows gathered from Xq through the row table, output
 // columns in logical gate | up order.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm_gate_up(GemmArgs g) { grouped_gemm_body<true>(g); }
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_gate_up(GemmArgs g) { grouped_gemm_body<true>(g); }
 // down projection: A = Hq in row-table order.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gemm_down(GemmArgs g) { grouped_gemm_body<false>(g); }
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_down(GemmArgs g) { grouped_gemm_body<false>(g); }
 
 // -------------------------------------------------------------- combine ---
 // y[t, :] = sum_j w[t, j] * dm[pos[t*k + j], :], j ascending, fma chain from 0.
@@ -615,7 +637,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     mark(L, kRouteQuant, st);
     hipLaunchKernelGGL(k_route_quant, dim3(n_route + nblk(xblocks * 8, 256)), dim3(256), 0, st,
                        L.logits, L.T, L.E, L.k, L.eidx, L.wts, L.mask, L.W, n_route, L.x, xblocks,
-                       L.xq, L.dx);
+                       L.d / 32, scale_stride(L.d), L.xq, L.dx);
     mark(L, kGroup, st);
     hipLaunchKernelGGL(k_group, dim3(L.E), dim3(kGroupThreads), 0, st, L.mask, L.W, L.E, L.wprefix,
                        L.counts, L.bounds, L.tiles, L.ntiles, L.done);
@@ -627,6 +649,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     GemmArgs gu;
     gu.A = L.xq;
     gu.A_scale = L.dx;
+    gu.a_scale_stride = scale_stride(L.d);
     gu.row_src = L.rtok;
     gu.blob = L.blob;
     gu.expert_stride = L.expert_stride;
@@ -645,11 +668,12 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     const int64_t hblocks = R * (L.f / 32);
     mark(L, kSwigluQ8, st);
     hipLaunchKernelGGL(k_swiglu_q8, dim3(nblk(hblocks * 8, 256)), dim3(256), 0, st, L.gu, R, L.f,
-                       L.hq, L.dh, L.h_out);
+                       L.hq, L.dh, scale_stride(L.f), L.h_out);
 
     GemmArgs dn = gu;
     dn.A = L.hq;
     dn.A_scale = L.dh;
+    dn.a_scale_stride = scale_stride(L.f);
     dn.row_src = nullptr;
     dn.q_off = L.d_q_off;
     dn.s_off = L.d_s_off;

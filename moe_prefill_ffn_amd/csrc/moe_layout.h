@@ -30,11 +30,14 @@ MOE_HD static inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a -
 //       byte i   (i < 4): low nibble K+i,    high nibble K+4+i
 //       byte 4+i (i < 4): low nibble K+8+i,  high nibble K+12+i
 //     nibble = w + 8  (w in [-8, 7] stored offset-binary)
-//   scales: for nt, pr, j < 32: 4 bytes at ((nt * K/64 + pr) * 32 + j) * 4 =
-//           fp16 scale of block 2pr, then of block 2pr+1, of row nt*32 + j.
+//   scales: in groups of kScaleGroup = 8 K-blocks (the last group zero-padded):
+//           for nt < N/32, g < ceil(K/256), j < 32: 16 bytes at
+//           ((nt * ceil(K/256) + g) * 32 + j) * 16 = fp16 scales of blocks
+//           8g .. 8g+7 of row nt*32 + j.
 //
 // One wave-wide 16-byte load per (n-tile, K pair) therefore hands every lane
-// exactly its B-operand bytes for two 32x32x32 int8 MFMAs.
+// exactly its B-operand bytes for two 32x32x32 int8 MFMAs, and one 512-byte load
+// (lanes 0-31) the n-tile's scales for eight blocks.
 //
 // W_gu's n-tiles interleave gate and up: n-tile 2i holds gate rows
 // [32 i, 32 i + 32), n-tile 2i+1 holds up rows [f + 32 i, f + 32 i + 32).
@@ -43,13 +46,20 @@ struct BlobLayout {
     uint64_t expert_bytes;
 };
 
+constexpr int kScaleGroup = 8;   // K-blocks per scale group
+
+// scale groups of a K extent, and the padded per-row stride (in blocks) of the
+// activation block-scale arrays the GEMMs read a whole group at a time from
+MOE_HD static inline int scale_groups(int K) { return (K / 32 + kScaleGroup - 1) / kScaleGroup; }
+MOE_HD static inline int scale_stride(int K) { return scale_groups(K) * kScaleGroup; }
+
 static inline BlobLayout blob_layout(int d, int f)
 {
     BlobLayout L;
     uint64_t n_gu_q = (uint64_t)2 * f * d / 2;
-    uint64_t n_gu_s = (uint64_t)2 * f * (d / 32) * 2;
+    uint64_t n_gu_s = (uint64_t)2 * f * scale_stride(d) * 2;
     uint64_t n_d_q = (uint64_t)d * f / 2;
-    uint64_t n_d_s = (uint64_t)d * (f / 32) * 2;
+    uint64_t n_d_s = (uint64_t)d * scale_stride(f) * 2;
     L.gu_q = 0;
     L.gu_s = L.gu_q + align_up(n_gu_q, 256);
     L.d_q = L.gu_s + align_up(n_gu_s, 256);
@@ -94,10 +104,10 @@ static inline WsLayout ws_layout(int d, int f, int E, int k, int Tmax)
     L.pos = take(R * 4);
     L.rtok = take(R * 4);
     L.xq = take((uint64_t)Tmax * d);
-    L.dx = take((uint64_t)Tmax * (d / 32) * 4);
+    L.dx = take((uint64_t)Tmax * scale_stride(d) * 4);   // [Tmax][scale_stride(d)]
     L.gu = take(R * 2 * f * 4);
     L.hq = take(R * f);
-    L.dh = take(R * (f / 32) * 4);
+    L.dh = take(R * scale_stride(f) * 4);                 // [R][scale_stride(f)]
     L.dm = take(R * d * 4);
     L.total = o;
     return L;

@@ -12,13 +12,12 @@ namespace moe {
 static bool pack_matrix(int N, int K, const int8_t* W, const uint16_t* S, int interleave_f,
                         uint8_t* q_dst, uint8_t* s_dst)
 {
-    const int npairs = K / 64, nbk = K / 32;
+    const int npairs = K / 64, nbk = K / 32, ngroups = scale_groups(K);
     for (int64_t i = 0; i < (int64_t)N * K; ++i)
         if (W[i] < -8 || W[i] > 7) return false;
     for (int nt = 0; nt < N / 32; ++nt) {
         for (int pr = 0; pr < npairs; ++pr) {
             uint8_t* qt = q_dst + ((int64_t)nt * npairs + pr) * 64 * 16;
-            uint32_t* st = reinterpret_cast<uint32_t*>(s_dst) + ((int64_t)nt * npairs + pr) * 32;
             for (int lane = 0; lane < 64; ++lane) {
                 const int j = lane & 31, h = lane >> 5;
                 const int n = interleave_f ? gu_logical_row(nt, j, interleave_f) : nt * 32 + j;
@@ -31,9 +30,15 @@ static bool pack_matrix(int N, int K, const int8_t* W, const uint16_t* S, int in
                         out[8 * q + 4 + i] = (uint8_t)((wr[k0 + 8 + i] + 8) | ((wr[k0 + 12 + i] + 8) << 4));
                     }
                 }
-                if (h == 0) {
-                    const uint16_t* sr = S + (int64_t)n * nbk;
-                    st[j] = (uint32_t)sr[2 * pr] | ((uint32_t)sr[2 * pr + 1] << 16);
+            }
+        }
+        for (int g = 0; g < ngroups; ++g) {
+            uint16_t* st = reinterpret_cast<uint16_t*>(s_dst) + ((int64_t)nt * ngroups + g) * 32 * kScaleGroup;
+            for (int j = 0; j < 32; ++j) {
+                const int n = interleave_f ? gu_logical_row(nt, j, interleave_f) : nt * 32 + j;
+                for (int b = 0; b < kScaleGroup; ++b) {
+                    const int blk = g * kScaleGroup + b;
+                    st[j * kScaleGroup + b] = blk < nbk ? S[(int64_t)n * nbk + blk] : (uint16_t)0;
                 }
             }
         }

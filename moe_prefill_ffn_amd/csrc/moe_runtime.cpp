@@ -518,26 +518,32 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
 
     // optional exports of the intermediate buffers
     const uint64_t R = (uint64_t)T * h->k;
+    // (rows x row_bytes, read with a source row stride of src_pitch bytes: the
+    // block-scale arrays are kept with a padded row stride in the workspace)
     struct Ex {
         void* dst;
-        uint64_t off, bytes;
+        uint64_t off, rows, row_bytes, src_pitch;
     } ex[] = {
-        {io.eidx, h->L.eidx, R * 4},
-        {io.weights, h->L.wts, R * 4},
-        {io.counts, h->L.counts, (uint64_t)h->E * 4},
-        {io.bounds, h->L.bounds, (uint64_t)(h->E + 1) * 4},
-        {io.rows, h->L.rows, R * 4},
-        {io.pos, h->L.pos, R * 4},
-        {io.xq, h->L.xq, (uint64_t)T * h->d},
-        {io.dx, h->L.dx, (uint64_t)T * (h->d / 32) * 4},
-        {io.gu, h->L.gu, R * 2 * h->f * 4},
-        {io.hq, h->L.hq, R * h->f},
-        {io.dh, h->L.dh, R * (h->f / 32) * 4},
-        {io.dm, h->L.dm, R * h->d * 4},
+        {io.eidx, h->L.eidx, 1, R * 4, R * 4},
+        {io.weights, h->L.wts, 1, R * 4, R * 4},
+        {io.counts, h->L.counts, 1, (uint64_t)h->E * 4, (uint64_t)h->E * 4},
+        {io.bounds, h->L.bounds, 1, (uint64_t)(h->E + 1) * 4, (uint64_t)(h->E + 1) * 4},
+        {io.rows, h->L.rows, 1, R * 4, R * 4},
+        {io.pos, h->L.pos, 1, R * 4, R * 4},
+        {io.xq, h->L.xq, 1, (uint64_t)T * h->d, (uint64_t)T * h->d},
+        {io.dx, h->L.dx, (uint64_t)T, (uint64_t)(h->d / 32) * 4, (uint64_t)scale_stride(h->d) * 4},
+        {io.gu, h->L.gu, 1, R * 2 * h->f * 4, R * 2 * h->f * 4},
+        {io.hq, h->L.hq, 1, R * h->f, R * h->f},
+        {io.dh, h->L.dh, R, (uint64_t)(h->f / 32) * 4, (uint64_t)scale_stride(h->f) * 4},
+        {io.dm, h->L.dm, 1, R * h->d * 4, R * h->d * 4},
     };
     for (const Ex& x : ex) {
-        if (!x.dst) continue;
-        e = hipMemcpyAsync(x.dst, h->ws + x.off, x.bytes, hipMemcpyDeviceToDevice, st);
+        if (!x.dst || x.rows == 0) continue;
+        if (x.rows == 1 || x.row_bytes == x.src_pitch)
+            e = hipMemcpyAsync(x.dst, h->ws + x.off, x.rows * x.row_bytes, hipMemcpyDeviceToDevice, st);
+        else
+            e = hipMemcpy2DAsync(x.dst, x.row_bytes, h->ws + x.off, x.src_pitch, x.row_bytes, x.rows,
+                                 hipMemcpyDeviceToDevice, st);
         if (e != hipSuccess) return hip_fail(h, e, "export copy");
     }
     h->stats.layers_run++;

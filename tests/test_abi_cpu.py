@@ -184,6 +184,7 @@ def test_oversized_struct_with_nonzero_tail_is_rejected():
 
 def _unpack_blob_matrix(buf: np.ndarray, N: int, K: int, interleave_f: int):
     """Read the tiled Q4 layout back, following the header's documented format."""
+    sx4 = lambda v: v - 8                        # offset-binary nibble
     npairs, nbk = K // 64, K // 32
     qs = buf[: N * K // 2].reshape(N // 32, npairs, 64, 16)
     W = np.zeros((N, K), np.int8)
@@ -196,15 +197,15 @@ def _unpack_blob_matrix(buf: np.ndarray, N: int, K: int, interleave_f: int):
                 for q in range(2):
                     k0 = 32 * (2 * pr + q) + 16 * h
                     for i in range(4):
-                        W[n, k0 + i] = (by[8 * q + i] & 15) - 8
-                        W[n, k0 + 4 + i] = (by[8 * q + i] >> 4) - 8
-                        W[n, k0 + 8 + i] = (by[8 * q + 4 + i] & 15) - 8
-                        W[n, k0 + 12 + i] = (by[8 * q + 4 + i] >> 4) - 8
+                        W[n, k0 + i] = sx4(by[8 * q + i] & 15)
+                        W[n, k0 + 4 + i] = sx4(by[8 * q + i] >> 4)
+                        W[n, k0 + 8 + i] = sx4(by[8 * q + 4 + i] & 15)
+                        W[n, k0 + 12 + i] = sx4(by[8 * q + 4 + i] >> 4)
     return W
 
 
-def test_pack_expert_layout_round_trip():
-    d, f = 128, 64
+@pytest.mark.parametrize("d,f", [(128, 64), (320, 192)])
+def test_pack_expert_layout_round_trip(d, f):
     r = np.random.default_rng(0)
     wgu_q = r.integers(-8, 8, (2 * f, d)).astype(np.int8)
     wgu_s = r.integers(0, 65535, (2 * f, d // 32)).astype(np.uint16)
@@ -213,20 +214,28 @@ def test_pack_expert_layout_round_trip():
     eb = mp.moe_prefill_expert_bytes(d, f)
     out = np.zeros(eb, np.uint8)
     mp.moe_prefill_pack_expert(d, f, wgu_q, wgu_s, wd_q, wd_s, out.ctypes.data)
+    ngd, ngf = -(-(d // 32) // 8), -(-(f // 32) // 8)     # 8-block scale groups
     gu_q_bytes = 2 * f * d // 2
     gu_s_off = gu_q_bytes
-    d_q_off = gu_s_off + ((2 * f * (d // 32) * 2 + 255) // 256) * 256
+    d_q_off = gu_s_off + ((2 * f * ngd * 8 * 2 + 255) // 256) * 256
     d_s_off = d_q_off + ((d * f // 2 + 255) // 256) * 256
+    assert eb == d_s_off + ((d * ngf * 8 * 2 + 255) // 256) * 256
     assert np.array_equal(_unpack_blob_matrix(out, 2 * f, d, f), wgu_q)
     assert np.array_equal(_unpack_blob_matrix(out[d_q_off:], d, f, 0), wd_q)
-    # scales: (nt, pr, j) -> [block 2pr, block 2pr+1]
-    sc = out[gu_s_off:gu_s_off + 2 * f * (d // 32) * 2].view(np.uint16).reshape(2 * f // 32, d // 64, 32, 2)
-    for nt in range(2 * f // 32):
-        rows = (f if nt % 2 else 0) + (nt // 2) * 32 + np.arange(32)
-        assert np.array_equal(sc[nt].transpose(1, 0, 2).reshape(32, -1), wgu_s[rows])
-    sd = out[d_s_off:d_s_off + d * (f // 32) * 2].view(np.uint16).reshape(d // 32, f // 64, 32, 2)
-    for nt in range(d // 32):
-        assert np.array_equal(sd[nt].transpose(1, 0, 2).reshape(32, -1), wd_s[nt * 32:(nt + 1) * 32])
+
+    def scales(sec, N, nbk, ng, row_of):
+        # (nt, group, j) -> 8 fp16 scales of blocks 8g .. 8g+7 (zero past the last block)
+        sc = sec.view(np.uint16).reshape(N // 32, ng, 32, 8)
+        for nt in range(N // 32):
+            rows = row_of(nt)
+            got = sc[nt].transpose(1, 0, 2).reshape(32, ng * 8)
+            assert np.array_equal(got[:, :nbk], rows)
+            assert not got[:, nbk:].any()
+
+    scales(out[gu_s_off:gu_s_off + 2 * f * ngd * 16], 2 * f, d // 32, ngd,
+           lambda nt: wgu_s[(f if nt % 2 else 0) + (nt // 2) * 32 + np.arange(32)])
+    scales(out[d_s_off:d_s_off + d * ngf * 16], d, f // 32, ngf,
+           lambda nt: wd_s[nt * 32:(nt + 1) * 32])
 
 
 def test_pack_rejects_out_of_range_weights():
