@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, published
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+VALU_PEAK_TOPS = 78.6        # fp32 VALU lane-ops/s: 256 CU x 4 SIMD x 32 lanes x 2.4 GHz (fma = 1 op)
 
 
 def log(*a):
@@ -140,18 +141,21 @@ def main() -> int:
     dn_tops = ops_dn / (dn_us * 1e-6) / 1e12
     q_bytes = T * E * 4 + R * 8 + T * d * 4 + T * d + T * (d // 32) * 4   # logits, eidx+w, X, Xq, dx
     c_bytes = R * d * 4 + R * 8 + T * d * 4
-    s_bytes = R * 2 * f * 4 + R * f + R * (f // 32) * 4
     traffic = load_traffic("gemm_gate_up", "resident")
     roofline = {
         "bound": "mfma", "achieved": round(gu_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
         "frac": round(gu_tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
         "kernel": "gemm_gate_up", "ops_per_launch": ops_gu, "mean_us": round(gu_us, 2),
         "dtype": "int8 x int4 -> int32 blocks, fp32 epilogue",
+        "note": "gate/up GEMM with the fused SwiGLU + Q8 epilogue (writes Hq, not GU)",
+        # the per-element fp32 block epilogue (convert + fma per output and 32-block) on the VALU:
+        # lane-ops / s against 256 CU x 4 SIMD x 32 lanes x 2.4 GHz
+        "valu_epilogue_Tops": round(2.0 * R * (2 * f) * (d // 32) / (gu_us * 1e-6) / 1e12, 2),
+        "valu_peak_Tops": VALU_PEAK_TOPS,
     }
     kernels = {n: (round(v, 2) if v is not None else None) for n, v in kern_us.items()}
     hbm = {
         "route_quant_GBs": round(q_bytes / (kern_us["route_quant"] * 1e-6) / 1e9, 1),
-        "swiglu_q8_GBs": round(s_bytes / (kern_us["swiglu_q8"] * 1e-6) / 1e9, 1),
         "combine_GBs": round(c_bytes / (kern_us["combine"] * 1e-6) / 1e9, 1),
         "gemm_down_TOPS": round(dn_tops, 2),
         "peak_GBs": HBM_PEAK_GBS,

@@ -245,16 +245,15 @@ int moe_prefill_get_stats(const moe_prefill_t* h, moe_stats_t* inout);
 
 /* ------------------------------------------------------------- tracing --- */
 
-#define MOE_N_KERNELS 7
+#define MOE_N_KERNELS 6
 /* Kernel ids, in launch order inside moe_prefill_run_layer. */
 enum {
     MOE_K_ROUTE_QUANT = 0,    /* top-k routing, router weights, membership mask; Xq = Q8(x) */
     MOE_K_GROUP = 1,          /* counts, group bounds, GEMM row tiles */
     MOE_K_SCATTER = 2,        /* row table */
-    MOE_K_GEMM_GATE_UP = 3,   /* GU grouped GEMM */
-    MOE_K_SWIGLU_Q8 = 4,      /* H = SwiGLU(GU), Hq = Q8(H) */
-    MOE_K_GEMM_DOWN = 5,      /* Dm grouped GEMM */
-    MOE_K_COMBINE = 6         /* y = weighted combine */
+    MOE_K_GEMM_GATE_UP = 3,   /* GU grouped GEMM with the SwiGLU + Q8 epilogue: Hq, its scales */
+    MOE_K_GEMM_DOWN = 4,      /* Dm grouped GEMM */
+    MOE_K_COMBINE = 5         /* y = weighted combine */
 };
 
 typedef struct moe_kernel_times {

@@ -73,7 +73,7 @@ class moe_stats_t(ctypes.Structure):
                 ("eff_depth", _i32), ("eff_residents", _i32), ("warnings", _i32)]
 
 
-MOE_N_KERNELS = 7
+MOE_N_KERNELS = 6
 
 
 class moe_kernel_times_t(ctypes.Structure):

@@ -15,7 +15,11 @@ struct GemmArgs {
     uint64_t q_off, s_off;    // matrix quant / scale section offsets in an expert
     const int32_t* tiles;     // [max_tiles][3]: expert, first row, end row
     const int32_t* ntiles;    // number of valid tiles (device)
-    float* out;               // [R, N]
+    float* out;               // [R, N]; gate/up launch: GU, written only if not null
+    int8_t* hq;               // gate/up launch: Hq [R, f] = Q8(SwiGLU(GU)) (else unused)
+    float* dh;                // gate/up launch: its block scales [R][dh_stride]
+    float* h_out;             // gate/up launch: optional H [R, f] (null: not written)
+    int dh_stride;
     int N, K;
     int E;                    // experts in the blob (tile expert indices are clamped to it)
     int gu_f;                 // f of the interleaved gate/up matrix (gate/up launch only)
@@ -48,16 +52,16 @@ struct LayerLaunch {
     float* dh;
     float* dm;
     float* h_out;             // optional export of H (nullptr: not written)
+    bool keep_gu;             // write GU to gu (for export)
     hipEvent_t* marks;        // optional: kNumKernels + 1 timing events (nullptr: none);
                               // marks[i] before kernel i, marks[kNumKernels] after the last
 };
 
 // kernel ids in launch order (timing)
-enum KernelId { kRouteQuant, kGroup, kScatter, kGemmGateUp, kSwigluQ8, kGemmDown, kCombine,
-                kNumKernels };
+enum KernelId { kRouteQuant, kGroup, kScatter, kGemmGateUp, kGemmDown, kCombine, kNumKernels };
 
-// route + quantise X, group (bounds, tiles, row table), GU GEMM, SwiGLU+Q8, down GEMM (last reader
-// of the weights) -- everything up to the combine.
+// route + quantise X, group (bounds, tiles, row table), GU GEMM with SwiGLU+Q8, down GEMM (last
+// reader of the weights) -- everything up to the combine.
 hipError_t launch_layer(const LayerLaunch& L, hipStream_t st);
 // combine (and clear the membership mask for the next layer)
 hipError_t launch_combine(const LayerLaunch& L, hipStream_t st);

@@ -184,34 +184,6 @@ __global__ __launch_bounds__(256) void k_route_quant(const float* __restrict__ l
     if (blk < n_blocks) quant_block8(x, blk, nbk, dx_stride, xq, dx);   // whole 8-lane groups together
 }
 
-// ---------------------------------------------------------- SwiGLU + Q8 ---
-// gu [R, 2f] (gate | up) -> h = silu(gate) * up -> Q8 blocks of 32 along f.
-__global__ __launch_bounds__(256) void k_swiglu_q8(const float* __restrict__ gu, int64_t R, int f,
-                                                   int8_t* __restrict__ hq, float* __restrict__ dh,
-                                                   int dh_stride, float* __restrict__ h_out)
-{
-    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int nbf = f >> 5;
-    const int64_t blk = g >> 3;
-    if (blk >= R * nbf) return;
-    const int sub = threadIdx.x & 7;
-    const int64_t r = blk / nbf;
-    const int b = (int)(blk - r * nbf);
-    const float* gr = gu + r * 2 * f + b * 32 + sub * 4;
-    const float4 gv = *reinterpret_cast<const float4*>(gr);
-    const float4 uv = *reinterpret_cast<const float4*>(gr + f);
-    float4 hv;
-    hv.x = gv.x / (1.0f + exp_cw(-gv.x)) * uv.x;
-    hv.y = gv.y / (1.0f + exp_cw(-gv.y)) * uv.y;
-    hv.z = gv.z / (1.0f + exp_cw(-gv.z)) * uv.z;
-    hv.w = gv.w / (1.0f + exp_cw(-gv.w)) * uv.w;
-    if (h_out) *reinterpret_cast<float4*>(h_out + r * f + b * 32 + sub * 4) = hv;
-    float d;
-    const uint32_t packed = q8_block_of8(hv, &d);
-    *reinterpret_cast<uint32_t*>(hq + r * f + b * 32 + sub * 4) = packed;
-    if (sub == 0) dh[r * dh_stride + b] = d;
-}
-
 // ---------------------------------------------------------------- group ---
 // The row table is a stable counting sort of the pairs p = t*k + j on their
 // expert.  Word w of expert e in the membership mask holds tokens 32w..32w+31
@@ -415,6 +387,65 @@ __device__ __forceinline__ int a_lds_off(int r, int c)
     return sr * 128 + ((((r & 1) << 2) | c) ^ (sr & 7)) * 16;
 }
 
+// Gate/up epilogue: SwiGLU + Q8 of the tile, fused.  Waves 2i and 2i+1 of the
+// workgroup hold the gate and up columns of f-block 2*ng + i (n-tiles interleave
+// gate and up).  The tile goes through LDS as fp32 [64 rows][kXsStride] (padded
+// so the MFMA-layout writes are bank-conflict free); then each 8-lane group
+// takes one (row, f-block): h = silu(gate) * up and its Q8 block, the same
+// arithmetic as the standalone SwiGLU + Q8 step.  GU and H are written out only
+// when asked for (g.out, g.h_out).
+constexpr int kXsStride = 136;            // floats per staged row (128 + 8 pad)
+
+__device__ __forceinline__ void swiglu_q8_epilogue(const GemmArgs& g, uint8_t* lds,
+                                                   const float (&acc0)[16], const float (&acc1)[16],
+                                                   int r0, int nrows, int ng, int nt)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, j32 = lane & 31;
+    if (g.out) {
+        const int col = gu_logical_row(nt, j32, g.gu_f);
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 8 * gq + 4 * h + i;
+                if (row < nrows) g.out[(int64_t)(r0 + row) * g.N + col] = acc0[4 * gq + i];
+                if (row + 32 < nrows) g.out[(int64_t)(r0 + row + 32) * g.N + col] = acc1[4 * gq + i];
+            }
+        }
+    }
+    float* xs = reinterpret_cast<float*>(lds);
+    __syncthreads();                                      // every wave is done with the ring
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * h + (i & 3);
+        xs[row * kXsStride + wave * 32 + j32] = acc0[i];
+        xs[(row + 32) * kXsStride + wave * 32 + j32] = acc1[i];
+    }
+    __syncthreads();
+    const int f = g.gu_f;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int t = it * 256 + tid;                     // (row, f-block of the pair, 4-column slice)
+        const int row = t >> 4, fb = (t >> 3) & 1, sub = t & 7;
+        if (row >= nrows) continue;                       // uniform over the 8-lane group
+        const float* xr = xs + row * kXsStride + fb * 64 + sub * 4;
+        const float4 gv = *reinterpret_cast<const float4*>(xr);
+        const float4 uv = *reinterpret_cast<const float4*>(xr + 32);
+        float4 hv;
+        hv.x = gv.x / (1.0f + exp_cw(-gv.x)) * uv.x;
+        hv.y = gv.y / (1.0f + exp_cw(-gv.y)) * uv.y;
+        hv.z = gv.z / (1.0f + exp_cw(-gv.z)) * uv.z;
+        hv.w = gv.w / (1.0f + exp_cw(-gv.w)) * uv.w;
+        const int64_t r = r0 + row;
+        const int fblk = 2 * ng + fb;
+        if (g.h_out) *reinterpret_cast<float4*>(g.h_out + r * f + fblk * 32 + sub * 4) = hv;
+        float d;
+        const uint32_t packed = q8_block_of8(hv, &d);
+        *reinterpret_cast<uint32_t*>(g.hq + r * f + fblk * 32 + sub * 4) = packed;
+        if (sub == 0) g.dh[r * g.dh_stride + fblk] = d;
+    }
+}
+
 template <bool kGateUp>
 __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
 {
@@ -437,8 +468,9 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
     const bool wave_on = nt_real < (N >> 5);
     const int nt = wave_on ? nt_real : (N >> 5) - 1;      // idle waves load valid memory
 
-    __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kStageBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t sbuf[2 * kScaleBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kRing * kStageBytes + 2 * kScaleBytes];
+    uint8_t* const ring = lds;
+    uint8_t* const sbuf = lds + kRing * kStageBytes;
 
     // ---- load sources (all addresses clamped in bounds)
     // A: this wave fills super-rows 8w..8w+7, lane -> super-row 8w + lane/8, slot lane%8
@@ -567,8 +599,12 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
         run(std::false_type{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped tail loads before exit
 
+    if (kGateUp) {
+        swiglu_q8_epilogue(g, lds, acc0, acc1, r0, nrows, ng, nt);
+        return;
+    }
     if (!wave_on) return;
-    const int col = kGateUp ? gu_logical_row(nt, j32, g.gu_f) : nt * 32 + j32;
+    const int col = nt * 32 + j32;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
 #pragma unroll
@@ -657,18 +693,17 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     gu.s_off = L.gu_s_off;
     gu.tiles = L.tiles;
     gu.ntiles = L.ntiles;
-    gu.out = L.gu;
+    gu.out = L.keep_gu ? L.gu : nullptr;
+    gu.hq = L.hq;
+    gu.dh = L.dh;
+    gu.dh_stride = scale_stride(L.f);
+    gu.h_out = L.h_out;
     gu.N = 2 * L.f;
     gu.K = L.d;
     gu.E = L.E;
     gu.gu_f = L.f;
     mark(L, kGemmGateUp, st);
     hipLaunchKernelGGL(k_gemm_gate_up, dim3(nblk(gu.N / 32, 4) * max_tiles_now), dim3(256), 0, st, gu);
-
-    const int64_t hblocks = R * (L.f / 32);
-    mark(L, kSwigluQ8, st);
-    hipLaunchKernelGGL(k_swiglu_q8, dim3(nblk(hblocks * 8, 256)), dim3(256), 0, st, L.gu, R, L.f,
-                       L.hq, L.dh, scale_stride(L.f), L.h_out);
 
     GemmArgs dn = gu;
     dn.A = L.hq;
@@ -678,6 +713,9 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     dn.q_off = L.d_q_off;
     dn.s_off = L.d_s_off;
     dn.out = L.dm;
+    dn.hq = nullptr;
+    dn.dh = nullptr;
+    dn.h_out = nullptr;
     dn.N = L.d;
     dn.K = L.f;
     dn.gu_f = 0;

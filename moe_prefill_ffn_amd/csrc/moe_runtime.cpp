@@ -480,6 +480,7 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
     LL.dh = reinterpret_cast<float*>(w + h->L.dh);
     LL.dm = reinterpret_cast<float*>(w + h->L.dm);
     LL.h_out = io.h;
+    LL.keep_gu = io.gu != nullptr;
     LL.marks = nullptr;
     std::array<hipEvent_t, kNumKernels + 1> tset{};
     if (h->timing) {
@@ -727,8 +728,9 @@ int moe_prefill_set_timing(moe_prefill_t* h, int32_t enable)
 
 const char* moe_prefill_kernel_name(int32_t id)
 {
+    static_assert(kNumKernels == MOE_N_KERNELS, "kernel ids of the header and the launcher agree");
     static const char* names[kNumKernels] = {"route_quant", "group", "row_scatter", "gemm_gate_up",
-                                             "swiglu_q8", "gemm_down", "combine"};
+                                             "gemm_down", "combine"};
     return (id >= 0 && id < kNumKernels) ? names[id] : "";
 }
 

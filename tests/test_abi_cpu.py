@@ -40,6 +40,15 @@ def test_library_exports_every_declared_symbol():
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error path")
+def test_kernel_ids_and_names():
+    names = [mp.lib().moe_prefill_kernel_name(i).decode() for i in range(mp.MOE_N_KERNELS)]
+    assert names == ["route_quant", "group", "row_scatter", "gemm_gate_up", "gemm_down", "combine"]
+    assert mp.lib().moe_prefill_kernel_name(mp.MOE_N_KERNELS) == b""
+    assert mp.lib().moe_prefill_kernel_name(-1) == b""
+    hdr = open(os.path.join(ROOT, "include", "moe_prefill.h")).read()
+    assert f"#define MOE_N_KERNELS {mp.MOE_N_KERNELS}" in hdr
+
+
 def test_create_without_gpu_fails_clearly():
     with pytest.raises(mp.MoePrefillError) as ei:
         mp.moe_prefill_create(256, 512, 8, 2, 64)

@@ -59,6 +59,42 @@ def test_edge_shapes(T, d, f, E, k, bias):
         assert (ref["counts"] == 0).sum() > 0     # the case really has empty experts
 
 
+@pytest.mark.parametrize("name", ["tiny", "resident"])
+def test_hot_path_without_intermediate_exports(name):
+    """The bench configuration: GU and H are not exported, so the gate/up GEMM
+    writes only Hq and its scales from the fused epilogue."""
+    w = wl.WORKLOADS[name]
+    say(f"[case] {name} exporting hq, dh only")
+    x, lg = wl.layer_activations(w, 0), wl.layer_logits(w, 0)
+    ex = ExpertCache(w, 0)
+    blob = host_blob(w, ex).cuda()
+    h = make_handle(w)
+    g = run_layer_gpu(h, w, x, lg, blob, exports=("hq", "dh", "rows"))
+    ref = oracle.layer(x, lg, w.k, ex, w.f)
+    h.close()
+    assert_equal("rows", g["rows"], ref["rows"])
+    assert_equal("hq", g["hq"], ref["hq"])
+    assert_equal("dh", g["dh"], ref["dh"])
+    assert_close("y", g["y"], ref["y"])
+
+
+def test_kernel_timing_reports_every_launch():
+    w = wl.WORKLOADS["tiny"]
+    say("[case] kernel timing")
+    x, lg = wl.layer_activations(w, 0), wl.layer_logits(w, 0)
+    blob = host_blob(w, ExpertCache(w, 0)).cuda()
+    h = make_handle(w)
+    mp.moe_prefill_set_timing(h, True)
+    for _ in range(3):
+        run_layer_gpu(h, w, x, lg, blob, exports=())
+    kt = mp.moe_prefill_kernel_times(h, reset=True)
+    mp.moe_prefill_set_timing(h, False)
+    h.close()
+    assert list(kt) == ["route_quant", "group", "row_scatter", "gemm_gate_up", "gemm_down", "combine"]
+    for name, (count, ms) in kt.items():
+        assert count == 3 and ms > 0.0, (name, count, ms)
+
+
 def test_tied_logits_pick_lowest_experts():
     w = wl.small_workload(40, 128, 128, 12, 4, seed_base=5)
     lg = np.zeros((w.T, w.E), np.float32)
