@@ -333,9 +333,8 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
 // K advances one packed pair (2 blocks, 64 K) per stage through a 4-deep LDS
 // ring filled by direct global->LDS loads (no register staging), issued three
 // stages ahead: per stage and wave 1 KiB of gathered A rows and the wave's
-// 1 KiB of packed Q4 weights.  A is stored as 128-byte "super-rows" (two
-// 64-byte rows) whose 16-byte chunks are XOR-swizzled by the super-row index,
-// which makes the MFMA operand reads bank-conflict free.  The block scales
+// 1 KiB of packed Q4 weights.  A's 16-byte chunks are XOR-swizzled within each
+// 64-byte row, which makes the MFMA operand reads bank-conflict free.  The block scales
 // come in groups of 8 blocks (4 stages) into a double-buffered LDS area, one
 // 16-byte load per lane: lanes 0-31 the fp16 scales of the wave's 32 weight
 // columns, lanes 32-63 the fp32 A scales of 16 rows (two lanes per row).
@@ -352,7 +351,7 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
 // 8 XCDs) receives a contiguous run of tiles: the n-groups of a row tile and
 // the row tiles of an expert share that XCD's L2.
 constexpr int kRing = 4;                  // LDS stages = stages per scale group
-constexpr int kA_OFF = 0;                 // [32 super-rows][8 chunks of 16 B], swizzled
+constexpr int kA_OFF = 0;                 // [64 rows][4 chunks of 16 B], chunks swizzled per row
 constexpr int kB_OFF = 4096;              // [4 waves][64 lanes][16 B]
 constexpr int kStageBytes = 8192;
 constexpr int kScaleBytes = 4096;         // [4 waves][ {32 cols x 8 fp16} | {16 rows x 8 fp32} ]
@@ -374,18 +373,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
     return __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
 }
-__device__ __forceinline__ void g2lds16(const void* g, const uint8_t* wave_base)
+// lds: wave-uniform LDS byte address of lane 0's destination
+__device__ __forceinline__ void g2lds16(const void* g, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds_addr(wave_base)) : "memory", "m0");
+                 :: "v"(g), "s"(lds) : "memory", "m0");
 }
 
-// byte offset of (row r, 16-byte chunk c < 4) of a stage's A tile
-__device__ __forceinline__ int a_lds_off(int r, int c)
-{
-    const int sr = r >> 1;
-    return sr * 128 + ((((r & 1) << 2) | c) ^ (sr & 7)) * 16;
-}
+// A tile of a stage: 64 rows x 64 bytes, row-major; 16-byte chunk c of row r
+// sits in slot c ^ a_swz(r).  Any 16 consecutive rows (one pass of a 128-bit
+// LDS read) then touch 16 distinct 16-byte bank groups, and any 8 consecutive
+// rows 8 distinct ones modulo 128 bytes.
+__device__ __forceinline__ int a_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__device__ __forceinline__ int a_lds_off(int r, int c) { return r * 64 + ((c ^ a_swz(r)) << 4); }
 
 // Gate/up epilogue: SwiGLU + Q8 of the tile, fused.  Waves 2i and 2i+1 of the
 // workgroup hold the gate and up columns of f-block 2*ng + i (n-tiles interleave
@@ -461,7 +461,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
     const int e = te < 0 ? 0 : (te >= g.E ? g.E - 1 : te); // always valid; a no-op for a sound list
     const int r0 = g.tiles[3 * tile + 1];
     const int nrows = g.tiles[3 * tile + 2] - r0;          // 1 .. kBM
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int K = g.K, N = g.N;
     const int npairs = K >> 6, ngroups = scale_groups(K);
     const int nt_real = ng * 4 + wave;
@@ -473,17 +474,15 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
     uint8_t* const sbuf = lds + kRing * kStageBytes;
 
     // ---- load sources (all addresses clamped in bounds)
-    // A: this wave fills super-rows 8w..8w+7, lane -> super-row 8w + lane/8, slot lane%8
+    // A: this wave fills rows 16w..16w+15, lane -> row 16w + lane/4, slot lane%4
     const int8_t* a_src;
     int a_col;
     {
-        const int sr = 8 * wave + (lane >> 3);
-        const int cis = (lane & 7) ^ (sr & 7);             // chunk-in-super-row held by this slot
-        const int row = 2 * sr + (cis >> 2);
+        const int row = 16 * wave + (lane >> 2);
         const int rr = r0 + (row < nrows ? row : nrows - 1);
         const int src = kGateUp ? g.row_src[rr] : rr;
         a_src = g.A + (int64_t)src * K;
-        a_col = (cis & 3) * 16;
+        a_col = ((lane & 3) ^ a_swz(row)) * 16;
     }
     const uint8_t* ex = g.blob + (uint64_t)e * g.expert_stride;
     const uint8_t* wq = ex + g.q_off + (uint64_t)nt * npairs * 1024 + lane * 16;
@@ -505,14 +504,15 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
 
     // stage = packed pair pr, scale group grp (clamped: tail loads repeat the
     // last one, never read)
-    auto issue_stage = [&](int pr, uint8_t* sb) {
+    const uint32_t lds_wave = lds_addr(lds) + wave * 1024;   // this wave's 1 KiB in each area
+    auto issue_stage = [&](int pr, int slot) {
         const int p = pr < npairs ? pr : npairs - 1;
-        g2lds16(a_src + p * 64 + a_col, sb + kA_OFF + wave * 1024);
-        g2lds16(wq + (uint64_t)p * 1024, sb + kB_OFF + wave * 1024);
+        g2lds16(a_src + p * 64 + a_col, lds_wave + slot * kStageBytes + kA_OFF);
+        g2lds16(wq + (uint64_t)p * 1024, lds_wave + slot * kStageBytes + kB_OFF);
     };
-    auto issue_scales = [&](int grp, uint8_t* sc) {
+    auto issue_scales = [&](int grp, int buf) {
         const int gg = grp < ngroups ? grp : ngroups - 1;
-        g2lds16(sc_src + (int64_t)gg * sc_step, sc + wave * 1024);
+        g2lds16(sc_src + (int64_t)gg * sc_step, lds_wave + kRing * kStageBytes + buf * kScaleBytes);
     };
 
     float acc0[16], acc1[16];
@@ -545,8 +545,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
         constexpr int kLater = 2 * (kRing - 2) + ((U == 1 || U == 2) ? 1 : 0);
         asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"(kLater) : "memory");
         const int grp = s >> 2;
-        if (U == 0) issue_scales(grp + 1, sbuf + ((grp + 1) & 1) * kScaleBytes);
-        issue_stage(s + kRing - 1, ring + ((U + kRing - 1) % kRing) * kStageBytes);
+        if (U == 0) issue_scales(grp + 1, (grp + 1) & 1);
+        issue_stage(s + kRing - 1, (U + kRing - 1) % kRing);
         if (!wave_on) return;
         const uint8_t* sb = ring + U * kStageBytes;
         const uint8_t* sc = sbuf + (grp & 1) * kScaleBytes;
@@ -583,9 +583,9 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
         }
     };
     auto run = [&](auto two_c) {
-        issue_scales(0, sbuf);
+        issue_scales(0, 0);
 #pragma unroll
-        for (int u = 0; u < kRing - 1; ++u) issue_stage(u, ring + u * kStageBytes);
+        for (int u = 0; u < kRing - 1; ++u) issue_stage(u, u);
         for (int s0 = 0; s0 < npairs; s0 += kRing) {
             stage(two_c, std::integral_constant<int, 0>{}, s0);
             if (s0 + 1 < npairs) stage(two_c, std::integral_constant<int, 1>{}, s0 + 1);
