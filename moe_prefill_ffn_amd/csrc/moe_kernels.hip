@@ -348,8 +348,10 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
 // waves per SIMD).
 //
 // Workgroups are numbered so that each XCD (dispatch is round-robin over the
-// 8 XCDs) receives a contiguous run of tiles: the n-groups of a row tile and
-// the row tiles of an expert share that XCD's L2.
+// 8 XCDs) receives a contiguous run of row tiles with all their n-groups: the
+// n-groups of a row tile and the row tiles of an expert share that XCD's L2.
+// Inside an XCD's run the gate/up launch takes the tiles of more than 32 rows
+// first, so its workgroups that start last are the cheaper half-height ones.
 constexpr int kRing = 4;                  // LDS stages = stages per scale group
 constexpr int kA_OFF = 0;                 // [64 rows][4 chunks of 16 B], chunks swizzled per row
 constexpr int kB_OFF = 4096;              // [4 waves][64 lanes][16 B]
@@ -450,12 +452,38 @@ template <bool kGateUp>
 __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
 {
     const int NG = ((g.N >> 5) + 3) >> 2;                 // n-groups of 4 n-tiles
-    const int n_act = *g.ntiles * NG;
-    const int L = blockIdx.x;
-    if (L >= n_act) return;                               // uniform across the workgroup
-    const int q8 = n_act >> 3, r8 = n_act & 7, xcd = L & 7, slot = L >> 3;
-    const int tau = xcd < r8 ? xcd * (q8 + 1) + slot : r8 * (q8 + 1) + (xcd - r8) * q8 + slot;
-    const int tile = tau / NG, ng = tau - tile * NG;
+    // XCD x (dispatch is round-robin over the 8 XCDs) takes a contiguous range of
+    // row tiles, all their n-groups (gate/up: the tiles of more than 32 rows first)
+    int tile, ng;
+    {
+        const int nt_all = *g.ntiles;
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        const int tq = nt_all >> 3, tr = nt_all & 7;
+        const int ta = xcd * tq + (xcd < tr ? xcd : tr);
+        const int tn = tq + (xcd < tr ? 1 : 0);
+        if (slot >= tn * NG) return;                      // uniform across the workgroup
+        if (kGateUp) {
+            int heavy = 0;
+            for (int t = ta; t < ta + tn; ++t) heavy += (g.tiles[3 * t + 2] - g.tiles[3 * t + 1]) > 32;
+            const bool want_heavy = slot < heavy * NG;
+            const int rel = want_heavy ? slot : slot - heavy * NG;
+            int k = rel / NG;
+            ng = rel - k * NG;
+            tile = ta;
+            for (int t = ta; t < ta + tn; ++t) {
+                if (((g.tiles[3 * t + 2] - g.tiles[3 * t + 1]) > 32) == want_heavy) {
+                    if (k == 0) {
+                        tile = t;
+                        break;
+                    }
+                    --k;
+                }
+            }
+        } else {
+            tile = ta + slot / NG;
+            ng = slot - (slot / NG) * NG;
+        }
+    }
 
     const int te = g.tiles[3 * tile + 0];
     const int e = te < 0 ? 0 : (te >= g.E ? g.E - 1 : te); // always valid; a no-op for a sound list
@@ -703,7 +731,8 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     gu.E = L.E;
     gu.gu_f = L.f;
     mark(L, kGemmGateUp, st);
-    hipLaunchKernelGGL(k_gemm_gate_up, dim3(nblk(gu.N / 32, 4) * max_tiles_now), dim3(256), 0, st, gu);
+    const unsigned tiles8 = 8 * nblk(max_tiles_now, 8);   // every XCD's tile range, rounded up
+    hipLaunchKernelGGL(k_gemm_gate_up, dim3(nblk(gu.N / 32, 4) * tiles8), dim3(256), 0, st, gu);
 
     GemmArgs dn = gu;
     dn.A = L.hq;
@@ -720,7 +749,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     dn.K = L.f;
     dn.gu_f = 0;
     mark(L, kGemmDown, st);
-    hipLaunchKernelGGL(k_gemm_down, dim3(nblk(dn.N / 32, 4) * max_tiles_now), dim3(256), 0, st, dn);
+    hipLaunchKernelGGL(k_gemm_down, dim3(nblk(dn.N / 32, 4) * tiles8), dim3(256), 0, st, dn);
     mark(L, kCombine, st);
     return hipGetLastError();
 }
