@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE prompt (prefill) FFN layer on one MI355X.
 
-One step = one whole layer through the C ABI (route, group, Xq, GU grouped
-GEMM, SwiGLU+requant, down grouped GEMM, combine) on the resident real-shape
+One step = one whole layer through the C ABI (route + Xq, group, row table,
+GU grouped GEMM with SwiGLU+requant, down grouped GEMM, combine) on the resident real-shape
 layer: T=1024 tokens, d_model=2048, d_ff=768, E=128 experts, top-8, Q4
 weights resident in HBM, synthetic seeded inputs.  The headline value is
 tokens/s per layer.
@@ -16,6 +16,12 @@ Also reported on the same line:
   streamed      the 4-layer streamed stack (same shape, 2-slot pool, depth-1
                 prefetch): tokens/s per pass, achieved H2D GB/s, measured PCIe
                 GB/s, fraction of copy time hidden and overlap efficiency
+  streamed_active_experts
+                the first three layers of the skewed stack (T=8192, d_model=4096,
+                d_ff=1536, E=256, Zipf routing) through a 2-slot pool:
+                whole-layer streaming with depth-1 prefetch against active_only
+                loads (only the routed experts, copied by a kernel after the
+                routing): ms and GB per pass
   cpu_baseline  the CPU oracle timed on this host's cores on the same layer
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -71,6 +77,7 @@ def main() -> int:
     ap.add_argument("--stream-passes", type=int, default=3)
     ap.add_argument("--cpu-reps", type=int, default=15)
     ap.add_argument("--no-stream", action="store_true")
+    ap.add_argument("--no-active", action="store_true", help="skip the active-expert streaming comparison")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 256 MiB device-to-device copies (counter scale reference)")
@@ -246,6 +253,61 @@ def main() -> int:
         log(f"[bench] streamed: {line['streamed']}")
         hs.close()
         del blobs
+        torch.cuda.empty_cache()
+
+    # ---- active-expert streaming: the first three layers of the skewed stack through a
+    # 2-slot pool, whole-layer streaming (depth-1 prefetch) against loading only the routed
+    # experts after routing
+    if not args.no_stream and not args.no_active:
+        wk = wl.WORKLOADS["skew"]
+        nl = 3
+        log(f"[bench] {wk.name}: packing {nl} pinned layer blobs")
+        lbk = mp.moe_prefill_layer_bytes(wk.d, wk.f, wk.E)
+        kblobs = []
+        for l in range(nl):
+            b = torch.empty(lbk, dtype=torch.uint8, pin_memory=True)
+            mp.pack_layer(wk.d, wk.f, wk.E, lambda e, l=l: wl.expert_weights(wk, l, e), b)
+            kblobs.append(b)
+        kx = [torch.from_numpy(wl.layer_activations(wk, l)).to(dev) for l in range(nl)]
+        klg = [torch.from_numpy(wl.layer_logits(wk, l)).to(dev) for l in range(nl)]
+        ky = torch.empty(wk.T, wk.d, device=dev)
+        hk = mp.moe_prefill_create(wk.d, wk.f, wk.E, wk.k, wk.T, device=0)
+
+        def passes(active: bool):
+            plan = mp.stream_pool_configure(hk, kblobs, prefetch_depth=1, resident_layers=0,
+                                            requested_slots=2, active_only=active)
+            for l in range(nl):            # first (cold) pass
+                mp.moe_prefill_run_layer(hk, kx[l], klg[l], ky, layer=l)
+            torch.cuda.synchronize()
+            s0 = mp.moe_prefill_get_stats(hk)
+            t0 = time.perf_counter()
+            for _ in range(args.stream_passes):
+                for l in range(nl):
+                    mp.moe_prefill_run_layer(hk, kx[l], klg[l], ky, layer=l)
+            torch.cuda.synchronize()
+            t = (time.perf_counter() - t0) / args.stream_passes
+            s1 = mp.moe_prefill_get_stats(hk)
+            moved = (s1["bytes_h2d"] - s0["bytes_h2d"] + s1["bytes_sparse"] - s0["bytes_sparse"]) / args.stream_passes
+            return plan, t, moved, (s1["experts_loaded"] - s0["experts_loaded"]) / args.stream_passes
+
+        plan_f, t_full, moved_f, _ = passes(False)
+        plan_a, t_act, moved_a, experts = passes(True)
+        line["streamed_active_experts"] = {
+            "workload": wk.name + f" (layers 0-{nl - 1})", "layers": nl,
+            "whole_layer": {"slots": plan_f["slots"], "depth": plan_f["depth"],
+                            "ms_per_pass": round(t_full * 1e3, 3), "GB_per_pass": round(moved_f / 1e9, 3),
+                            "h2d_GBs_achieved": round(moved_f / t_full / 1e9, 2),
+                            "tokens_per_s_per_pass": round(wk.T / t_full, 1)},
+            "active_only": {"slots": plan_a["slots"], "depth": plan_a["depth"],
+                            "ms_per_pass": round(t_act * 1e3, 3), "GB_per_pass": round(moved_a / 1e9, 3),
+                            "h2d_GBs_achieved": round(moved_a / t_act / 1e9, 2),
+                            "experts_per_pass": experts, "experts_total": nl * wk.E,
+                            "tokens_per_s_per_pass": round(wk.T / t_act, 1)},
+            "speedup": round(t_full / t_act, 3),
+        }
+        log(f"[bench] active-expert streaming: {line['streamed_active_experts']}")
+        hk.close()
+        del kblobs, kx, klg, ky
         torch.cuda.empty_cache()
 
     # ---- CPU oracle on the host's cores, same resident layer (bounded: a few full layers)

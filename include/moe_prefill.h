@@ -186,6 +186,11 @@ typedef struct stream_pool_params {
     int32_t eff_residents;           /* resident leading layers */
     int32_t warnings;                /* MOE_WARN_* bits */
     int32_t reserved0;
+    /* appended fields (a smaller struct_size leaves them 0) */
+    int32_t active_only;             /* != 0: a streamed layer that is not in the pool is
+                                        loaded after its routing, only the experts that
+                                        received rows; no lookahead prefetch (eff_depth 0) */
+    int32_t reserved1;
 } stream_pool_params_t;
 
 #define MOE_WARN_SLOT_OVER_BUDGET 1  /* the one mandatory slot exceeds max_vram_bytes */
@@ -202,6 +207,14 @@ typedef struct stream_pool_params {
  *    allocation failure fewer slots of the same size are tried (residents
  *    first, then depth) down to one; if one slot fails: MOE_ENOMEM;
  *  - resident layers are uploaded before returning;
+ *  - active_only (the survey's "active-expert-only streaming"): the layer's
+ *    routing decides its copy.  After the grouping step of moe_prefill_run_layer
+ *    a kernel reads the experts with rows > 0 straight from the pinned host blob
+ *    (PCIe reads by the GPU, no host round trip) into the slot; experts without
+ *    rows are not copied and never read.  host_blobs must then be page-locked
+ *    host memory mapped for the device (hipHostMalloc, torch pin_memory);
+ *    anything else is MOE_EINVAL.  The slot then holds a partial layer, so a
+ *    later run of the same layer loads again;
  *  - calling again first drains the copy stream and releases the previous
  *    pool, prefetches and residents.
  * Effective values are written back into *inout.
@@ -237,23 +250,30 @@ typedef struct moe_stats {
     uint64_t prefetch_activated;     /* layers that found their prefetched slot */
     uint64_t sync_loads;             /* load-then-compute copies */
     uint64_t prefetch_failed;        /* prefetch enqueues that failed (fell back) */
-    uint64_t bytes_h2d;              /* bytes copied into the pool */
+    uint64_t bytes_h2d;              /* bytes copied into the pool by whole-layer copies */
     int32_t eff_slots, eff_depth, eff_residents, warnings;
+    /* appended fields */
+    uint64_t sparse_loads;           /* active-expert loads launched */
+    uint64_t experts_loaded;         /* experts those loads copied (device-counted) */
+    uint64_t bytes_sparse;           /* bytes they copied (device-counted) */
 } moe_stats_t;
 
+/* Counters of the handle.  experts_loaded and bytes_sparse are kept on the
+ * device; reading them waits for the device to finish its queued work. */
 int moe_prefill_get_stats(const moe_prefill_t* h, moe_stats_t* inout);
 
 /* ------------------------------------------------------------- tracing --- */
 
-#define MOE_N_KERNELS 6
+#define MOE_N_KERNELS 7
 /* Kernel ids, in launch order inside moe_prefill_run_layer. */
 enum {
     MOE_K_ROUTE_QUANT = 0,    /* top-k routing, router weights, membership mask; Xq = Q8(x) */
     MOE_K_GROUP = 1,          /* counts, group bounds, GEMM row tiles */
-    MOE_K_SCATTER = 2,        /* row table */
-    MOE_K_GEMM_GATE_UP = 3,   /* GU grouped GEMM with the SwiGLU + Q8 epilogue: Hq, its scales */
-    MOE_K_GEMM_DOWN = 4,      /* Dm grouped GEMM */
-    MOE_K_COMBINE = 5         /* y = weighted combine */
+    MOE_K_EXPERT_LOAD = 2,    /* active-expert load of a streamed layer (active_only pools) */
+    MOE_K_SCATTER = 3,        /* row table */
+    MOE_K_GEMM_GATE_UP = 4,   /* GU grouped GEMM with the SwiGLU + Q8 epilogue: Hq, its scales */
+    MOE_K_GEMM_DOWN = 5,      /* Dm grouped GEMM */
+    MOE_K_COMBINE = 6         /* y = weighted combine */
 };
 
 typedef struct moe_kernel_times {
@@ -265,7 +285,9 @@ typedef struct moe_kernel_times {
 
 /* enable != 0: every kernel of the following moe_prefill_run_layer calls is
  * bracketed by HIP events recorded on the launch stream (one event record
- * between consecutive kernels); 0 stops it.  Host only. */
+ * between consecutive kernels); 0 stops it.  Host only.  A kernel that a
+ * layer does not launch (the expert load outside active_only loads) is not
+ * counted for that layer. */
 int moe_prefill_set_timing(moe_prefill_t* h, int32_t enable);
 
 /* Waits (bounded; MOE_ETIMEOUT) for the timed launches so far, adds their

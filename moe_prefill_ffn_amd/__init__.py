@@ -56,7 +56,8 @@ class stream_pool_params_t(ctypes.Structure):
     _fields_ = [("struct_size", _u32), ("n_layers", _i32), ("host_blobs", ctypes.POINTER(_vp)),
                 ("layer_bytes", _u64), ("prefetch_depth", _i32), ("resident_layers", _i32),
                 ("max_vram_bytes", _i64), ("requested_slots", _i32), ("eff_slots", _i32),
-                ("eff_depth", _i32), ("eff_residents", _i32), ("warnings", _i32), ("reserved0", _i32)]
+                ("eff_depth", _i32), ("eff_residents", _i32), ("warnings", _i32), ("reserved0", _i32),
+                ("active_only", _i32), ("reserved1", _i32)]
 
 
 class moe_pool_plan_t(ctypes.Structure):
@@ -70,10 +71,11 @@ class moe_stats_t(ctypes.Structure):
     _fields_ = [("struct_size", _u32), ("reserved0", _i32), ("layers_run", _u64),
                 ("prefetch_queued", _u64), ("prefetch_activated", _u64), ("sync_loads", _u64),
                 ("prefetch_failed", _u64), ("bytes_h2d", _u64), ("eff_slots", _i32),
-                ("eff_depth", _i32), ("eff_residents", _i32), ("warnings", _i32)]
+                ("eff_depth", _i32), ("eff_residents", _i32), ("warnings", _i32),
+                ("sparse_loads", _u64), ("experts_loaded", _u64), ("bytes_sparse", _u64)]
 
 
-MOE_N_KERNELS = 6
+MOE_N_KERNELS = 7
 
 
 class moe_kernel_times_t(ctypes.Structure):
@@ -297,8 +299,9 @@ def moe_prefill_run_layer(handle: Handle, x: torch.Tensor, logits: torch.Tensor,
 
 def stream_pool_configure(handle: Handle, host_blobs: Sequence[torch.Tensor], prefetch_depth: int = 1,
                           resident_layers: int = 0, max_vram_bytes: int = 0,
-                          requested_slots: int = 0) -> dict:
-    """Plan + allocate the slot pool over pinned host blobs (one per layer)."""
+                          requested_slots: int = 0, active_only: bool = False) -> dict:
+    """Plan + allocate the slot pool over pinned host blobs (one per layer).
+    active_only: streamed layers are loaded after their routing, only the experts with rows."""
     p = stream_pool_params_t()
     p.struct_size = ctypes.sizeof(p)
     n = len(host_blobs)
@@ -316,6 +319,7 @@ def stream_pool_configure(handle: Handle, host_blobs: Sequence[torch.Tensor], pr
     p.resident_layers = resident_layers
     p.max_vram_bytes = max_vram_bytes
     p.requested_slots = requested_slots
+    p.active_only = 1 if active_only else 0
     _check(lib().stream_pool_configure(handle.ptr, ctypes.byref(p)), handle.ptr)
     handle._pool_keep = list(host_blobs)
     return dict(slots=p.eff_slots, depth=p.eff_depth, residents=p.eff_residents, warnings=p.warnings)

@@ -51,6 +51,9 @@ struct LayerLaunch {
     int8_t* hq;
     float* dh;
     float* dm;
+    const uint8_t* load_src;  // active-expert load: device-accessible pinned host blob of the
+    uint8_t* load_dst;        // layer and its pool slot (load_src null: the blob is in place)
+    unsigned long long* load_stats;   // [2] experts and bytes loaded (device counters)
     float* h_out;             // optional export of H (nullptr: not written)
     bool keep_gu;             // write GU to gu (for export)
     hipEvent_t* marks;        // optional: kNumKernels + 1 timing events (nullptr: none);
@@ -58,10 +61,12 @@ struct LayerLaunch {
 };
 
 // kernel ids in launch order (timing)
-enum KernelId { kRouteQuant, kGroup, kScatter, kGemmGateUp, kGemmDown, kCombine, kNumKernels };
+enum KernelId { kRouteQuant, kGroup, kExpertLoad, kScatter, kGemmGateUp, kGemmDown, kCombine,
+                kNumKernels };
 
-// route + quantise X, group (bounds, tiles, row table), GU GEMM with SwiGLU+Q8, down GEMM (last
-// reader of the weights) -- everything up to the combine.
+// route + quantise X, group (bounds, tiles), the active-expert load (if load_src), the row table,
+// GU GEMM with SwiGLU+Q8, down GEMM (last reader of the weights) -- everything up to the combine.
+// The kExpertLoad mark is recorded whether or not that kernel runs.
 hipError_t launch_layer(const LayerLaunch& L, hipStream_t st);
 // combine (and clear the membership mask for the next layer)
 hipError_t launch_combine(const LayerLaunch& L, hipStream_t st);

@@ -298,6 +298,35 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(const uint32_t* __restr
     }
 }
 
+// -------------------------------------------------------- expert load ---
+// Active-expert load of a streamed layer: once the grouping has counted the
+// rows of every expert, copy only the experts that received rows from the
+// pinned host blob (read over PCIe by the kernel itself, so the choice needs no
+// host round trip) into the pool slot.  Every workgroup takes a grid-stride
+// share of each active expert's 16-byte words, expert after expert.
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void k_expert_load(const uint8_t* __restrict__ src,
+                                                     uint8_t* __restrict__ dst,
+                                                     const int32_t* __restrict__ counts, int E,
+                                                     uint64_t expert_bytes,
+                                                     unsigned long long* __restrict__ stats)
+{
+    const uint64_t n16 = expert_bytes / 16;
+    const uint64_t stride = (uint64_t)gridDim.x * 256;
+    for (int e = 0; e < E; ++e) {
+        if (counts[e] == 0) continue;                     // uniform
+        const v4u* s = reinterpret_cast<const v4u*>(src + (uint64_t)e * expert_bytes);
+        v4u* d = reinterpret_cast<v4u*>(dst + (uint64_t)e * expert_bytes);
+        for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride)
+            d[i] = __builtin_nontemporal_load(s + i);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            atomicAdd(&stats[0], 1ull);
+            atomicAdd(&stats[1], (unsigned long long)expert_bytes);
+        }
+    }
+}
+
 // Row table: pair p = t*k + j goes to row bounds[e] + prefix[e][t/32] + (tokens
 // of word t/32 before t routed to e) -- stable in p.
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eidx, int64_t R, int k,
@@ -705,6 +734,10 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     mark(L, kGroup, st);
     hipLaunchKernelGGL(k_group, dim3(L.E), dim3(kGroupThreads), 0, st, L.mask, L.W, L.E, L.wprefix,
                        L.counts, L.bounds, L.tiles, L.ntiles, L.done);
+    mark(L, kExpertLoad, st);
+    if (L.load_src)
+        hipLaunchKernelGGL(k_expert_load, dim3(512), dim3(256), 0, st, L.load_src, L.load_dst, L.counts,
+                           L.E, L.expert_stride, L.load_stats);
     mark(L, kScatter, st);
     hipLaunchKernelGGL(k_scatter, dim3(nblk(R, 256)), dim3(256), 0, st, L.eidx, R, L.k, L.mask,
                        L.wprefix, L.bounds, L.W, L.rows, L.pos, L.rtok);

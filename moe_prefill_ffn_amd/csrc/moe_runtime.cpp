@@ -39,6 +39,8 @@ struct moe_prefill {
     bool pool_on = false;
     int nl = 0;
     std::vector<const void*> blobs;
+    bool active_only = false;
+    std::vector<const uint8_t*> blobs_dev;   // device addresses of the pinned host blobs (active_only)
     uint64_t layer_bytes = 0, slot_bytes = 0;
     PoolShape shape;
     int warnings = 0;
@@ -54,7 +56,12 @@ struct moe_prefill {
 
     // kernel timing
     bool timing = false;
-    std::vector<std::array<hipEvent_t, kNumKernels + 1>> t_pending, t_free;
+    struct TimedLayer {
+        std::array<hipEvent_t, kNumKernels + 1> ev{};
+        uint32_t launched = 0;          // bit i: kernel i ran in this layer
+    };
+    std::vector<TimedLayer> t_pending;
+    std::vector<std::array<hipEvent_t, kNumKernels + 1>> t_free;
     uint64_t t_launches[kNumKernels] = {};
     double t_ms[kNumKernels] = {};
 };
@@ -254,6 +261,8 @@ void pool_release(moe_prefill_t* h)
     h->pool_on = false;
     h->nl = 0;
     h->blobs.clear();
+    h->blobs_dev.clear();
+    h->active_only = false;
     h->slot_layer.clear();
     h->layer_slot.clear();
     h->ev_ready.clear();
@@ -364,6 +373,7 @@ int moe_prefill_create(const moe_prefill_params_t* pin, moe_prefill_t** out)
     e = hipStreamCreateWithFlags(&h->copy, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipMemset(h->ws + h->L.mask, 0, (size_t)h->E * h->L.W * 4);
     if (e == hipSuccess) e = hipMemset(h->ws + h->L.done, 0, 4);
+    if (e == hipSuccess) e = hipMemset(h->ws + h->L.load_stats, 0, 16);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         const int rc = hip_fail(nullptr, e, "create");
@@ -383,9 +393,10 @@ void moe_prefill_destroy(moe_prefill_t* h)
     {
         DevGuard guard(h->dev);
         pool_release(h);
-        for (auto* v : {&h->t_pending, &h->t_free})
-            for (auto& set : *v)
-                for (hipEvent_t e : set) (void)hipEventDestroy(e);
+        for (auto& set : h->t_pending)
+            for (hipEvent_t e : set.ev) (void)hipEventDestroy(e);
+        for (auto& set : h->t_free)
+            for (hipEvent_t e : set) (void)hipEventDestroy(e);
         if (h->copy) (void)hipStreamDestroy(h->copy);
         if (h->ws_owned && h->ws) (void)hipFree(h->ws);
     }
@@ -409,7 +420,7 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
     DevGuard guard(h->dev);
 
     const uint8_t* blob = nullptr;
-    int slot = -1;
+    int slot = -1, sparse_slot = -1;
     hipError_t e = hipSuccess;
     if (io.layer < 0) {
         if (!io.weights_dev) return fail(h, MOE_EINVAL, "layer == -1 needs weights_dev");
@@ -425,6 +436,16 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
                 h->stats.prefetch_activated++;
                 h->from_prefetch[slot] = 0;
             }
+        } else if (h->active_only) {
+            // active-expert load: the kernels of this layer fill the slot after routing
+            slot = pick_victim(h, io.layer, -1);
+            if (slot < 0) return fail(h, MOE_ESTATE, "no pool slot available");
+            const int old = h->slot_layer[slot];
+            if (old >= 0) h->layer_slot[old] = -1;
+            h->slot_layer[slot] = -1;                     // a partial layer: never reused as whole
+            if (h->free_set[slot]) e = hipStreamWaitEvent(st, h->ev_free[slot], 0);
+            sparse_slot = slot;
+            h->stats.sparse_loads++;
         } else {
             // load-then-compute: a stream-ordered copy into a free slot first
             slot = pick_victim(h, io.layer, -1);
@@ -456,6 +477,9 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
     LL.logits = io.logits;
     LL.y = io.y;
     LL.blob = blob;
+    LL.load_src = sparse_slot >= 0 ? h->blobs_dev[io.layer] : nullptr;
+    LL.load_dst = sparse_slot >= 0 ? h->pool + (uint64_t)sparse_slot * h->slot_bytes : nullptr;
+    LL.load_stats = reinterpret_cast<unsigned long long*>(w + h->L.load_stats);
     LL.expert_stride = h->B.expert_bytes;
     LL.gu_q_off = h->B.gu_q;
     LL.gu_s_off = h->B.gu_s;
@@ -515,7 +539,12 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
         h->mask_dirty = true;
         return hip_fail(h, e, "combine launch");
     }
-    if (h->timing) h->t_pending.push_back(tset);
+    if (h->timing) {
+        moe_prefill::TimedLayer tl;
+        tl.ev = tset;
+        tl.launched = ((1u << kNumKernels) - 1) & ~(sparse_slot >= 0 ? 0u : 1u << kExpertLoad);
+        h->t_pending.push_back(tl);
+    }
 
     // optional exports of the intermediate buffers
     const uint64_t R = (uint64_t)T * h->k;
@@ -633,9 +662,27 @@ int stream_pool_configure(moe_prefill_t* h, stream_pool_params_t* inout)
     for (int i = 0; i < p.n_layers; ++i)
         if (!p.host_blobs[i]) return fail(h, MOE_EINVAL, "pool: null host blob");
 
+    // active_only: the kernel reads the host blobs itself, so they must be page-locked host memory
+    // mapped for the device; its device address is taken from the runtime
+    std::vector<const uint8_t*> blobs_dev;
+    if (p.active_only) {
+        for (int i = 0; i < p.n_layers; ++i) {
+            hipPointerAttribute_t at{};
+            const hipError_t e = hipPointerGetAttributes(&at, p.host_blobs[i]);
+            if (e != hipSuccess || at.type != hipMemoryTypeHost || !at.devicePointer) {
+                (void)hipGetLastError();
+                return fail(h, MOE_EINVAL, "pool: active_only needs pinned host blobs mapped for the device");
+            }
+            const uint8_t* dp = static_cast<const uint8_t*>(at.devicePointer);
+            if (reinterpret_cast<uintptr_t>(dp) % 16)
+                return fail(h, MOE_EINVAL, "pool: active_only needs 16-byte aligned host blobs");
+            blobs_dev.push_back(dp);
+        }
+    }
     const uint64_t slot_bytes = align_up(p.layer_bytes, 1 << 16);
     int warn = 0;
-    PoolShape s = plan_initial(p.n_layers, slot_bytes, p.prefetch_depth, p.resident_layers,
+    const int want_depth = p.active_only ? 0 : p.prefetch_depth;   // routing decides the copy: no lookahead
+    PoolShape s = plan_initial(p.n_layers, slot_bytes, want_depth, p.resident_layers,
                                p.max_vram_bytes, p.requested_slots, &warn);
     const char* cap_env = getenv("MOE_TEST_POOL_MAX_SLOTS");
     const int cap = cap_env ? atoi(cap_env) : 0;
@@ -657,13 +704,15 @@ int stream_pool_configure(moe_prefill_t* h, stream_pool_params_t* inout)
             write_struct(inout, p);
             return fail(h, MOE_ENOMEM, "pool: the mandatory one-slot pool could not be allocated");
         }
-        s = plan_degrade(s, p.n_layers, p.prefetch_depth, p.resident_layers, &warn);
+        s = plan_degrade(s, p.n_layers, want_depth, p.resident_layers, &warn);
     }
 
     h->pool = pool;
     h->pool_on = true;
     h->nl = p.n_layers;
     h->blobs.assign(p.host_blobs, p.host_blobs + p.n_layers);
+    h->active_only = p.active_only != 0;
+    h->blobs_dev = blobs_dev;
     h->layer_bytes = p.layer_bytes;
     h->slot_bytes = slot_bytes;
     h->shape = s;
@@ -729,8 +778,8 @@ int moe_prefill_set_timing(moe_prefill_t* h, int32_t enable)
 const char* moe_prefill_kernel_name(int32_t id)
 {
     static_assert(kNumKernels == MOE_N_KERNELS, "kernel ids of the header and the launcher agree");
-    static const char* names[kNumKernels] = {"route_quant", "group", "row_scatter", "gemm_gate_up",
-                                             "gemm_down", "combine"};
+    static const char* names[kNumKernels] = {"route_quant", "group", "expert_load", "row_scatter",
+                                             "gemm_gate_up", "gemm_down", "combine"};
     return (id >= 0 && id < kNumKernels) ? names[id] : "";
 }
 
@@ -742,16 +791,17 @@ int moe_prefill_kernel_times(moe_prefill_t* h, moe_kernel_times_t* inout, int32_
     if (!read_struct(inout, &out, &why)) return fail(h, MOE_EINVAL, why);
     DevGuard guard(h->dev);
     for (auto& set : h->t_pending) {
-        const int rc = wait_event(h, set[kNumKernels]);
+        const int rc = wait_event(h, set.ev[kNumKernels]);
         if (rc != MOE_OK) return rc;
         for (int i = 0; i < kNumKernels; ++i) {
+            if (!(set.launched >> i & 1u)) continue;      // not launched in that layer
             float ms = 0.0f;
-            if (hipEventElapsedTime(&ms, set[i], set[i + 1]) == hipSuccess) {
+            if (hipEventElapsedTime(&ms, set.ev[i], set.ev[i + 1]) == hipSuccess) {
                 h->t_ms[i] += ms;
                 h->t_launches[i]++;
             }
         }
-        h->t_free.push_back(set);
+        h->t_free.push_back(set.ev);
     }
     h->t_pending.clear();
     out.n_kernels = kNumKernels;
@@ -773,7 +823,17 @@ int moe_prefill_get_stats(const moe_prefill_t* h, moe_stats_t* inout)
     moe_stats_t tmp;
     std::string why;
     if (!read_struct(inout, &tmp, &why)) return fail(nullptr, MOE_EINVAL, why);
-    write_struct(inout, h->stats);
+    moe_stats_t out = h->stats;
+    if (out.sparse_loads) {   // the device-side counters of the active-expert loads
+        unsigned long long c[2] = {0, 0};
+        DevGuard guard(h->dev);
+        hipError_t e = hipDeviceSynchronize();
+        if (e == hipSuccess) e = hipMemcpy(c, h->ws + h->L.load_stats, sizeof(c), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(const_cast<moe_prefill_t*>(h), e, "stats read");
+        out.experts_loaded = c[0];
+        out.bytes_sparse = c[1];
+    }
+    write_struct(inout, out);
     return MOE_OK;
 }
 

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error path")
 def test_kernel_ids_and_names():
     names = [mp.lib().moe_prefill_kernel_name(i).decode() for i in range(mp.MOE_N_KERNELS)]
-    assert names == ["route_quant", "group", "row_scatter", "gemm_gate_up", "gemm_down", "combine"]
+    assert names == ["route_quant", "group", "expert_load", "row_scatter", "gemm_gate_up", "gemm_down", "combine"]
     assert mp.lib().moe_prefill_kernel_name(mp.MOE_N_KERNELS) == b""
     assert mp.lib().moe_prefill_kernel_name(-1) == b""
     hdr = open(os.path.join(ROOT, "include", "moe_prefill.h")).read()

@@ -172,3 +172,74 @@ def test_streamed_real_shape_stack_matches_resident_and_oracle():
     ref = oracle.layer(wl.layer_activations(w, 2), wl.layer_logits(w, 2), w.k, ExpertCache(w, 2, keep=False),
                        w.f, tokens=toks)
     assert_close("streamed layer 2 y", outs[2][1][toks], ref["y"])
+
+
+# ------------------------------------------------------ active-expert loads ---
+
+@pytest.fixture(scope="module")
+def skew4():
+    say("[case] 4-layer skewed stack (many empty experts)")
+    w = wl.Workload("stack4_T96_d256_f320_E48_top2_zipf", 96, 256, 320, 48, 2, 4, 700, bias=("zipf", 1.1))
+    return Stack(w, 4)
+
+
+def _active_experts(st, layer):
+    lg = wl.layer_logits(st.w, layer)
+    top = np.argsort(-lg, axis=1, kind="stable")[:, :st.w.k]
+    return np.unique(top).size
+
+
+def test_active_only_loads_only_routed_experts(skew4):
+    h = make_handle(skew4.w)
+    plan = _configure(h, skew4, prefetch_depth=2, resident_layers=0, requested_slots=2, active_only=True)
+    assert plan["depth"] == 0 and plan["residents"] == 0      # routing decides the copy: no lookahead
+    outs = skew4.run_passes(h, 2)
+    skew4.check(outs)                                         # identical to the resident run
+    s = mp.moe_prefill_get_stats(h)
+    active = sum(_active_experts(skew4, l) for l in range(4))
+    assert active < 4 * skew4.w.E                             # the case has idle experts
+    eb = mp.moe_prefill_expert_bytes(skew4.w.d, skew4.w.f)
+    assert s["sparse_loads"] == 8 and s["sync_loads"] == 0 and s["prefetch_queued"] == 0
+    assert s["experts_loaded"] == 2 * active
+    assert s["bytes_sparse"] == 2 * active * eb
+    assert s["bytes_h2d"] == 0
+    h.close()
+
+
+def test_active_only_one_slot_reuse_and_residents(skew4):
+    """One streaming slot rewritten by every layer (experts a layer does not use
+    keep the previous layer's bytes and are never read), plus a resident layer
+    that is uploaded whole and never reloaded."""
+    h = make_handle(skew4.w)
+    lb = skew4.blobs[0].numel()
+    slot = (lb + 65535) // 65536 * 65536
+    plan = _configure(h, skew4, prefetch_depth=1, resident_layers=1, max_vram_bytes=2 * slot,
+                      active_only=True)
+    assert (plan["slots"], plan["depth"], plan["residents"]) == (2, 0, 1)
+    skew4.check(skew4.run_passes(h, 2, order=[0, 2, 1, 3, 2]))
+    s = mp.moe_prefill_get_stats(h)
+    assert s["sparse_loads"] == 2 * 4                         # every non-resident run loads again
+    h.close()
+
+
+def test_active_only_rejects_pageable_blobs(skew4):
+    h = make_handle(skew4.w)
+    pageable = [b.clone() for b in skew4.blobs]               # ordinary host memory
+    assert not pageable[0].is_pinned()
+    with pytest.raises(mp.MoePrefillError) as ei:
+        _raw_configure(h, pageable)                           # rejected before any kernel runs
+    assert ei.value.code == mp.MOE_EINVAL
+    h.close()
+
+
+def _raw_configure(h, blobs):
+    """Calls the C entry point directly (the binding itself refuses unpinned tensors)."""
+    import ctypes
+    p = mp.stream_pool_params_t()
+    p.struct_size = ctypes.sizeof(p)
+    arr = (ctypes.c_void_p * len(blobs))(*[b.data_ptr() for b in blobs])
+    p.n_layers = len(blobs)
+    p.host_blobs = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    p.layer_bytes = blobs[0].numel()
+    p.active_only = 1
+    mp._check(mp.lib().stream_pool_configure(h.ptr, ctypes.byref(p)), h.ptr)
