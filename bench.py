@@ -22,6 +22,11 @@ Also reported on the same line:
                 whole-layer streaming with depth-1 prefetch against active_only
                 loads (only the routed experts, copied by a kernel after the
                 routing): ms and GB per pass
+  stacks        the two whole streamed stacks: 48 layers at T=3072 (4 resident
+                leading layers, depth-2 prefetch, 7-slot budget) and the skewed 8-layer
+                stack (3 slots, depth 2): tokens/s per pass, H2D GB/s achieved against
+                the measured PCIe rate, copy-hidden fraction, overlap efficiency, and
+                the resident per-layer kernel times and GEMM rates at those shapes
   cpu_baseline  the CPU oracle timed on this host's cores on the same layer
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -69,6 +74,220 @@ def load_traffic(kernel: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def pack_blobs(mp, wl, torch, w, pinned: bool = True):
+    """Pinned host blobs of every layer of workload w (generated and packed on the host cores)."""
+    lb = mp.moe_prefill_layer_bytes(w.d, w.f, w.E)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    blobs = []
+    for l in range(w.n_layers):
+        b = torch.empty(lb, dtype=torch.uint8, pin_memory=pinned)
+        mp.pack_layer(w.d, w.f, w.E, lambda e, l=l: wl.expert_weights(w, l, e), b, threads=threads)
+        blobs.append(b)
+    return blobs, lb
+
+
+def stack_leg(mp, wl, torch, dev, key: str, passes: int) -> dict:
+    """One whole streamed stack: pass time through the slot pool with the workload's depth,
+    slot count and VRAM budget, against the copy-only time (every streamed layer's blob over
+    PCIe) and the compute-only time (every layer resident in HBM)."""
+    w = wl.WORKLOADS[key]
+    st = w.stream
+    log(f"[bench] {w.name}: packing {w.n_layers} pinned layer blobs")
+    t0 = time.perf_counter()
+    blobs, lb = pack_blobs(mp, wl, torch, w)
+    log(f"[bench] packed {w.n_layers} x {lb / 2**20:.0f} MiB in {time.perf_counter() - t0:.1f} s")
+    xs = [torch.from_numpy(wl.layer_activations(w, l)).to(dev) for l in range(w.n_layers)]
+    lgs = [torch.from_numpy(wl.layer_logits(w, l)).to(dev) for l in range(w.n_layers)]
+    y = torch.empty(w.T, w.d, device=dev)
+    h = mp.moe_prefill_create(w.d, w.f, w.E, w.k, w.T, device=0)
+    R = w.T * w.k
+    # compute only: all layers resident, per-kernel device times
+    devb = [b.to(dev) for b in blobs]
+    for l in range(w.n_layers):
+        mp.moe_prefill_run_layer(h, xs[l], lgs[l], y, layer=-1, weights=devb[l])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(passes):
+        for l in range(w.n_layers):
+            mp.moe_prefill_run_layer(h, xs[l], lgs[l], y, layer=-1, weights=devb[l])
+    torch.cuda.synchronize()
+    t_comp_all = (time.perf_counter() - t0) / passes
+    mp.moe_prefill_set_timing(h, True)
+    for l in range(w.n_layers):
+        mp.moe_prefill_run_layer(h, xs[l], lgs[l], y, layer=-1, weights=devb[l])
+    torch.cuda.synchronize()
+    kt = mp.moe_prefill_kernel_times(h, reset=True)
+    mp.moe_prefill_set_timing(h, False)
+    kern_us = {n: (ms / c * 1e3 if c else None) for n, (c, ms) in kt.items()}
+    gu_tops = 2.0 * R * (2 * w.f) * w.d / (kern_us["gemm_gate_up"] * 1e-6) / 1e12
+    dn_tops = 2.0 * R * w.d * w.f / (kern_us["gemm_down"] * 1e-6) / 1e12
+    del devb
+    torch.cuda.empty_cache()
+    budget = st.budget_slots * lb if st.budget_slots else 0
+    plan = mp.stream_pool_configure(h, blobs, prefetch_depth=st.depth, resident_layers=st.residents,
+                                    max_vram_bytes=budget, requested_slots=st.slots)
+    streamed = w.n_layers - plan["residents"]
+    # copy only: the streamed layers' blobs, back to back on one stream (best of 2)
+    dst = torch.empty(lb, dtype=torch.uint8, device=dev)
+    t_copy = 1e9
+    for _ in range(2):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for b in blobs[plan["residents"]:]:
+            dst.copy_(b, non_blocking=True)
+        torch.cuda.synchronize()
+        t_copy = min(t_copy, time.perf_counter() - t0)
+    del dst
+    torch.cuda.empty_cache()
+    for l in range(w.n_layers):            # first (cold) pass
+        mp.moe_prefill_run_layer(h, xs[l], lgs[l], y, layer=l)
+    torch.cuda.synchronize()
+    s0 = mp.moe_prefill_get_stats(h)
+    t_pass = []
+    for _ in range(passes):
+        t0 = time.perf_counter()
+        for l in range(w.n_layers):
+            mp.moe_prefill_run_layer(h, xs[l], lgs[l], y, layer=l)
+        torch.cuda.synchronize()
+        t_pass.append(time.perf_counter() - t0)
+    # the median pass: the host's PCIe share varies from pass to pass on a shared node
+    t_wall = sorted(t_pass)[len(t_pass) // 2]
+    s1 = mp.moe_prefill_get_stats(h)
+    moved = (s1["bytes_h2d"] - s0["bytes_h2d"]) / passes
+    pcie = streamed * lb / t_copy
+    hidden = max(0.0, t_copy + t_comp_all - t_wall)
+    out = {
+        "workload": w.name, "layers": w.n_layers, "slots": plan["slots"], "depth": plan["depth"],
+        "residents": plan["residents"], "streamed_layers": streamed,
+        "tokens_per_s_per_pass": round(w.T / t_wall, 1), "ms_per_pass": round(t_wall * 1e3, 3),
+        "ms_per_pass_all": [round(t * 1e3, 3) for t in t_pass],
+        "h2d_GB_per_pass": round(moved / 1e9, 3), "h2d_GBs_achieved": round(moved / t_wall / 1e9, 2),
+        "pcie_h2d_GBs_measured": round(pcie / 1e9, 2),
+        "pcie_roofline_frac": round((moved / pcie) / t_wall, 4) if pcie > 0 else None,
+        "copy_ms_per_pass": round(t_copy * 1e3, 3), "compute_ms_per_pass": round(t_comp_all * 1e3, 3),
+        "copy_hidden_frac": round(hidden / t_copy, 4) if t_copy > 0 else None,
+        "overlap_efficiency": round(hidden / min(t_copy, t_comp_all), 4) if t_copy > 0 else None,
+        "prefetch_activated": (s1["prefetch_activated"] - s0["prefetch_activated"]) / passes,
+        "sync_loads": (s1["sync_loads"] - s0["sync_loads"]) / passes,
+        "resident_layer": {
+            "us_per_layer": round(t_comp_all * 1e6 / w.n_layers, 1),
+            "tokens_per_s_per_layer": round(w.T * w.n_layers / t_comp_all, 1),
+            "kernels_us": {n: (round(v, 2) if v is not None else None) for n, v in kern_us.items()},
+            "gemm_gate_up_TOPS": round(gu_tops, 2), "gemm_gate_up_frac": round(gu_tops / INT8_PEAK_TOPS, 4),
+            "gemm_down_TOPS": round(dn_tops, 2), "gemm_down_frac": round(dn_tops / INT8_PEAK_TOPS, 4),
+        },
+    }
+    h.close()
+    del blobs, xs, lgs, y
+    torch.cuda.empty_cache()
+    return out
+
+
+STACK_KEYS = ("stream48", "skew")
+
+
+def trace_windows(wl, passes: int):
+    """Per stack of the --stacks-only run: the half-open range of layer ordinals (counted
+    over the whole run, in launch order) that are the timed streamed passes.  Each layer
+    is one k_route_quant ... k_combine sequence; per stack the run does 1 + passes + 1
+    compute-only passes, one cold streamed pass, then the timed streamed passes."""
+    out, base = {}, 0
+    for key in STACK_KEYS:
+        n = wl.WORKLOADS[key].n_layers
+        first = base + n * (passes + 2) + n
+        out[key] = (first, first + n * passes)
+        base = first + n * passes
+    return out
+
+
+def _intervals_union(iv):
+    iv = sorted(iv)
+    out = []
+    for a, b in iv:
+        if out and a <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], b)
+        else:
+            out.append([a, b])
+    return out
+
+
+def _overlap(u1, u2):
+    i = j = 0
+    tot = 0
+    while i < len(u1) and j < len(u2):
+        a = max(u1[i][0], u2[j][0])
+        b = min(u1[i][1], u2[j][1])
+        if b > a:
+            tot += b - a
+        if u1[i][1] < u2[j][1]:
+            i += 1
+        else:
+            j += 1
+    return tot
+
+
+def summarize_trace(trace_dir: str, passes: int) -> dict:
+    """Copy/compute overlap of the timed streamed passes, from rocprofv3's kernel and
+    memory-copy traces of a `bench.py --stacks-only` run."""
+    import csv
+    import glob
+
+    import workload as wl
+
+    def one(pattern):
+        f = sorted(glob.glob(os.path.join(trace_dir, "**", pattern), recursive=True))
+        if not f:
+            raise FileNotFoundError(f"no {pattern} under {trace_dir}")
+        return list(csv.DictReader(open(f[0])))
+
+    kern = one("*kernel_trace.csv")
+    copies = one("*memory_copy_trace.csv")
+    kiv = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in kern]
+    kiv.sort()
+    rq = [iv for iv in kiv if iv[2].startswith("k_route_quant") or "k_route_quant" in iv[2]]
+    cb = [iv for iv in kiv if "k_combine" in iv[2]]
+    h2d = []
+    for r in copies:
+        dirn = r.get("Direction", "") + r.get("Operation", "") + r.get("Kind", "")
+        if "HOST_TO_DEVICE" in dirn.upper() or "H2D" in dirn.upper():
+            nbytes = None
+            for key in ("Bytes", "Size", "Copy_Bytes"):
+                if key in r and r[key] not in ("", None):
+                    nbytes = int(r[key])
+            h2d.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), nbytes))
+    res = {}
+    for key, (lo, hi) in trace_windows(wl, passes).items():
+        if hi > len(rq) or hi > len(cb):
+            res[key] = {"error": f"trace has {len(rq)} layers, window needs {hi}"}
+            continue
+        w0, w1 = rq[lo][0], cb[hi - 1][1]
+        ku = _intervals_union([(a, b) for a, b, _ in kiv if b > w0 and a < w1])
+        cin = [(max(a, w0), min(b, w1), n) for a, b, n in h2d if b > w0 and a < w1]
+        cu = _intervals_union([(a, b) for a, b, _ in cin])
+        copy_ns = sum(b - a for a, b in cu)
+        kern_ns = sum(b - a for a, b in ku)
+        hid = _overlap(cu, ku)
+        nb = [n for _, _, n in cin]
+        bytes_ = sum(nb) if nb and all(n is not None for n in nb) else None
+        wall = (w1 - w0) / passes
+        gaps = [cu[i + 1][0] - cu[i][1] for i in range(len(cu) - 1)]
+        res[key] = {
+            "window_ms_per_pass": round(wall / 1e6, 3),
+            "h2d_copies": len(cin) / passes,
+            "copy_busy_ms_per_pass": round(copy_ns / passes / 1e6, 3),
+            "kernel_busy_ms_per_pass": round(kern_ns / passes / 1e6, 3),
+            "copy_hidden_frac": round(hid / copy_ns, 4) if copy_ns else None,
+            "kernel_time_under_copies_frac": round(hid / kern_ns, 4) if kern_ns else None,
+            "h2d_GB_per_pass": round(bytes_ / passes / 1e9, 3) if bytes_ is not None else None,
+            "h2d_GBs_over_window": round(bytes_ / (w1 - w0), 2) if bytes_ is not None else None,
+            "h2d_GBs_while_copying": round(bytes_ / copy_ns, 2) if bytes_ and copy_ns else None,
+            "copy_gap_ms": {"mean": round(sum(gaps) / len(gaps) / 1e6, 4) if gaps else None,
+                            "max": round(max(gaps) / 1e6, 4) if gaps else None,
+                            "total_per_pass": round(sum(gaps) / passes / 1e6, 3)},
+        }
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -79,6 +298,12 @@ def main() -> int:
     ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--no-active", action="store_true", help="skip the active-expert streaming comparison")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-stacks", action="store_true", help="skip the 48-layer and skewed 8-layer stacks")
+    ap.add_argument("--stack-passes", type=int, default=3)
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="summarise rocprofv3 kernel + memory-copy traces of a --stacks-only run")
+    ap.add_argument("--stacks-only", action="store_true",
+                    help="only the two whole streamed stacks (for traces of the streaming)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 256 MiB device-to-device copies (counter scale reference)")
     args = ap.parse_args()
@@ -86,6 +311,10 @@ def main() -> int:
         print("bench.py measures one GPU: the MoE prefill FFN path here runs on a single "
               "MI355X (no layer split, no collectives); run it with --gpus 1", file=sys.stderr)
         return 2
+
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace, args.stack_passes), indent=1))
+        return 0
 
     import numpy as np
     import torch
@@ -102,6 +331,10 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_launch": src.numel() * 4, "launches": 5}))
+        return 0
+    if args.stacks_only:
+        out = {key: stack_leg(mp, wl, torch, dev, key, args.stack_passes) for key in STACK_KEYS}
+        print(json.dumps({"stacks": out}), flush=True)
         return 0
     w = wl.WORKLOADS["resident"]
     T, d, f, E, k = w.T, w.d, w.f, w.E, w.k
@@ -309,6 +542,15 @@ def main() -> int:
         hk.close()
         del kblobs, kx, klg, ky
         torch.cuda.empty_cache()
+
+    # ---- whole streamed stacks: the 48-layer prompt stack (T=3072, 4 resident leading layers,
+    # depth 2) and the skewed 8-layer stack (T=8192, d_model=4096, d_ff=1536, E=256, 3 slots,
+    # depth 2), each with its compute-only (all layers resident) and copy-only times
+    if not args.no_stream and not args.no_stacks:
+        line["stacks"] = {}
+        for key in STACK_KEYS:
+            line["stacks"][key] = stack_leg(mp, wl, torch, dev, key, args.stack_passes)
+            log(f"[bench] stack {key}: {line['stacks'][key]}")
 
     # ---- CPU oracle on the host's cores, same resident layer (bounded: a few full layers)
     if not args.no_cpu:

@@ -157,6 +157,7 @@ class Handle:
         if self.ptr:
             lib().moe_prefill_destroy(self.ptr)
             self.ptr = None
+        self._pool_keep = []
 
     def __enter__(self):
         return self
