@@ -372,9 +372,11 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
 // gives the scale products a_scale[row] * w_scale[col] of both row halves (one
 // rounding each, as a plain fp32 multiply), and per row half one
 // v_mfma_i32_32x32x32_i8 gives the exact int32 block sums.  The VALU is left
-// with unpacking the nibbles and the convert + fma per element.  The row halves
-// are processed one after the other, which keeps a wave under 128 VGPRs (four
-// waves per SIMD).
+// with unpacking the nibbles and the convert + fma per element.  Both row
+// halves' integer MFMAs are issued before the first half's convert + fma, so the
+// second one runs under that VALU work; a wave stays at 122 VGPRs (four waves
+// per SIMD).  A partly filled half converts only the 8-row register groups that
+// hold rows of the tile.
 //
 // Workgroups are numbered so that each XCD (dispatch is round-robin over the
 // 8 XCDs) receives a contiguous run of row tiles with all their n-groups: the
@@ -590,11 +592,24 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
     const int ws_off = wave * 1024 + j32 * 16;
     const int xs_off = (lane >> 4) * 1024 + 512 + (lane & 15) * 32;
 
+    // acc[i] += (float)is[i] * t[off + i] for the register groups that hold tile rows: element
+    // i of a lane is row 8*(i/4) + 4*h + i%4 of its half, so group g = i/4 covers rows
+    // 8g .. 8g+7 (the first kG groups; kG = 0: the first G, known only at run time)
+    auto fma_groups = [&](auto full_c, float(&acc)[16], const v16i& is, const v32f& t, int off, int G) {
+        constexpr int kG = decltype(full_c)::value;     // groups fixed at compile time (0: G)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            if (kG ? g < kG : g < G) {
+#pragma unroll
+                for (int i = 4 * g; i < 4 * g + 4; ++i) acc[i] = __builtin_fmaf((float)is[i], t[off + i], acc[i]);
+            }
+        }
+    };
     // one stage (U = position in the scale group): wait for its loads, sync,
     // queue the stage three ahead into the slot freed by the previous stage
     // (and, at a group start, the next group's scales), then two blocks of
     // MFMA + epilogue
-    auto stage = [&](auto two_c, auto u_c, int s) {
+    auto stage = [&](auto two_c, auto full_c, auto u_c, int s, int G) {
         constexpr bool kTwo = decltype(two_c)::value;
         constexpr int U = decltype(u_c)::value;
         // loads issued after this stage's: two per later stage in flight, plus the
@@ -623,37 +638,46 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
             const float dw = (float)__builtin_bit_cast(_Float16, hb);
             // t[16*half + i] = a_scale(row of D element i in that half) * w_scale(col)
             const v32f t = __builtin_amdgcn_mfma_f32_32x32x1f32(q ? dx.y : dx.x, dw, fzero, 0, 0, 0);
-            {
-                const v4i a = *reinterpret_cast<const v4i*>(sb + kA_OFF + a_off0[q]);
-                const v16i is = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop, zero, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc0[i] = __builtin_fmaf((float)is[i], t[i], acc0[i]);
-            }
-            __builtin_amdgcn_sched_barrier(0);   // keep the halves apart: low register pressure
+            const v4i a0 = *reinterpret_cast<const v4i*>(sb + kA_OFF + a_off0[q]);
+            v16i is0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bop, zero, 0, 0, 0);
             if (kTwo) {
-                const v4i a = *reinterpret_cast<const v4i*>(sb + kA_OFF + a_off1[q]);
-                const v16i is = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bop, zero, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc1[i] = __builtin_fmaf((float)is[i], t[16 + i], acc1[i]);
+                const v4i a1 = *reinterpret_cast<const v4i*>(sb + kA_OFF + a_off1[q]);
+                const v16i is1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, bop, zero, 0, 0, 0);
+                // empty: orders the second MFMA before the first half's VALU work
+                asm volatile("" : "+v"(is0) : "v"(is1));
+                fma_groups(std::integral_constant<int, 4>{}, acc0, is0, t, 0, G);
+                fma_groups(full_c, acc1, is1, t, 16, G);
+            } else {
+                fma_groups(std::integral_constant<int, 0>{}, acc0, is0, t, 0, G);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    auto run = [&](auto two_c) {
+    // the partly filled row half (the second of two, or the only one) runs only the 8-row
+    // register groups that hold rows of the tile
+    auto run = [&](auto two_c, auto full_c) {
+        constexpr bool kTwo = decltype(two_c)::value;
+        const int G = ((kTwo ? nrows - 32 : nrows) + 7) >> 3;
         issue_scales(0, 0);
 #pragma unroll
         for (int u = 0; u < kRing - 1; ++u) issue_stage(u, u);
         for (int s0 = 0; s0 < npairs; s0 += kRing) {
-            stage(two_c, std::integral_constant<int, 0>{}, s0);
-            if (s0 + 1 < npairs) stage(two_c, std::integral_constant<int, 1>{}, s0 + 1);
-            if (s0 + 2 < npairs) stage(two_c, std::integral_constant<int, 2>{}, s0 + 2);
-            if (s0 + 3 < npairs) stage(two_c, std::integral_constant<int, 3>{}, s0 + 3);
+            stage(two_c, full_c, std::integral_constant<int, 0>{}, s0, G);
+            if (s0 + 1 < npairs) stage(two_c, full_c, std::integral_constant<int, 1>{}, s0 + 1, G);
+            if (s0 + 2 < npairs) stage(two_c, full_c, std::integral_constant<int, 2>{}, s0 + 2, G);
+            if (s0 + 3 < npairs) stage(two_c, full_c, std::integral_constant<int, 3>{}, s0 + 3, G);
         }
     };
-    if (nrows > 32)
-        run(std::true_type{});
+    if (nrows > 56)
+        run(std::true_type{}, std::integral_constant<int, 4>{});
+    else if (nrows > 48)
+        run(std::true_type{}, std::integral_constant<int, 3>{});
+    else if (nrows > 40)
+        run(std::true_type{}, std::integral_constant<int, 2>{});
+    else if (nrows > 32)
+        run(std::true_type{}, std::integral_constant<int, 1>{});
     else
-        run(std::false_type{});
+        run(std::false_type{}, std::integral_constant<int, 0>{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped tail loads before exit
 
     if (kGateUp) {

@@ -59,6 +59,25 @@ def test_edge_shapes(T, d, f, E, k, bias):
         assert (ref["counts"] == 0).sum() > 0     # the case really has empty experts
 
 
+def test_tile_row_counts_at_every_group_boundary():
+    """Experts with row counts on both sides of every 8-row register group of a
+    GEMM row tile (1 .. 97 rows: one and two 32-row halves, partly filled halves of
+    1-4 groups, full tiles plus a tail): k = 1 and each token's logit for its
+    assigned expert raised by 12, so the counts are exact."""
+    counts = [1, 7, 8, 9, 16, 17, 24, 25, 31, 32, 33, 40, 41, 48, 49, 56, 57, 63, 64, 65, 72, 97]
+    E, k, d, f = len(counts) + 2, 1, 128, 192         # two experts get no rows
+    T = sum(counts)
+    w = wl.small_workload(T, d, f, E, k, seed_base=4242)
+    owner = np.repeat(np.arange(len(counts)), counts)
+    rng = np.random.default_rng(5)
+    owner = owner[rng.permutation(T)]
+    lg = wl.layer_logits(w, 0).copy()
+    lg[np.arange(T), owner] += 12.0
+    g, ref = _full_case(w, lg=lg)
+    assert list(ref["counts"][:len(counts)]) == counts and ref["counts"][-2:].sum() == 0
+    check_full_parity(w, g, ref)
+
+
 @pytest.mark.parametrize("name", ["tiny", "resident"])
 def test_hot_path_without_intermediate_exports(name):
     """The bench configuration: GU and H are not exported, so the gate/up GEMM
