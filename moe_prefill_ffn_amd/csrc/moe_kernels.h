@@ -44,7 +44,6 @@ struct LayerLaunch {
     int32_t* rows;
     int32_t* pos;
     int32_t* rtok;
-    uint32_t* done;           // grouping hand-off counter (zero between layers)
     int8_t* xq;
     float* dx;
     float* gu;

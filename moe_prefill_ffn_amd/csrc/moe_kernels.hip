@@ -189,24 +189,16 @@ __global__ __launch_bounds__(256) void k_route_quant(const float* __restrict__ l
 // expert.  Word w of expert e in the membership mask holds tokens 32w..32w+31
 // routed to e.
 //
-// k_group: one workgroup per expert computes the exclusive prefix of the word
-// popcounts and the expert's row count.  The last workgroup to finish (a
-// device-scope counter, release/acquire fences around it) then computes the
-// group bounds (exclusive scan of the counts) and the GEMM row-tile list
-// (expert, first row, end row; kBM rows per tile; expert order), and resets the
-// counter for the next layer.
+// k_group: one workgroup per expert writes the exclusive prefix of the word
+// popcounts and the expert's row count.  No workgroup waits for another: the
+// bounds are derived from the counts by every workgroup of the next kernel.
 constexpr int kGroupThreads = 256;
 
 __global__ __launch_bounds__(kGroupThreads) void k_group(const uint32_t* __restrict__ mask, int W,
-                                                         int E, int32_t* __restrict__ wprefix,
-                                                         int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ bounds,
-                                                         int32_t* __restrict__ tiles,
-                                                         int32_t* __restrict__ ntiles,
-                                                         uint32_t* __restrict__ done)
+                                                         int32_t* __restrict__ wprefix,
+                                                         int32_t* __restrict__ counts)
 {
     __shared__ int s_tot[4];
-    __shared__ int s_last;
     const int e = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int running = 0;
@@ -231,71 +223,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(const uint32_t* __restr
         running += total;
         __syncthreads();
     }
-    if (tid == 0) {
-        counts[e] = running;
-        __threadfence();                                  // publish counts[e] device-wide
-        s_last = atomicAdd(done, 1u) == (uint32_t)(E - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();                                      // see every workgroup's counts
-
-    // last workgroup: bounds and tiles, 4 experts per thread (E <= 1024)
-    int c4[4], t4[4], sc = 0, st = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ee = tid * 4 + i;
-        c4[i] = ee < E ? __hip_atomic_load(&counts[ee], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-        t4[i] = (c4[i] + kBM - 1) / kBM;
-        sc += c4[i];
-        st += t4[i];
-    }
-    int ic = sc, it = st;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int yc = __shfl_up(ic, o);
-        const int yt = __shfl_up(it, o);
-        if (lane >= o) {
-            ic += yc;
-            it += yt;
-        }
-    }
-    __shared__ int s_wc[4], s_wt[4];
-    if (lane == 63) {
-        s_wc[wave] = ic;
-        s_wt[wave] = it;
-    }
-    __syncthreads();
-    int bc = 0, bt = 0, all_c = 0, all_t = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        bc += i < wave ? s_wc[i] : 0;
-        bt += i < wave ? s_wt[i] : 0;
-        all_c += s_wc[i];
-        all_t += s_wt[i];
-    }
-    int start = bc + ic - sc, tstart = bt + it - st;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ee = tid * 4 + i;
-        if (ee < E) {
-            bounds[ee] = start;
-            for (int q = 0; q < t4[i]; ++q) {
-                const int r0 = start + q * kBM;
-                const int r1 = r0 + kBM < start + c4[i] ? r0 + kBM : start + c4[i];
-                tiles[3 * (tstart + q) + 0] = ee;
-                tiles[3 * (tstart + q) + 1] = r0;
-                tiles[3 * (tstart + q) + 2] = r1;
-            }
-        }
-        start += c4[i];
-        tstart += t4[i];
-    }
-    if (tid == 0) {
-        bounds[E] = all_c;
-        *ntiles = all_t;
-        *done = 0u;                                       // ready for the next layer
-    }
+    if (tid == 0) counts[e] = running;
 }
 
 // -------------------------------------------------------- expert load ---
@@ -328,21 +256,103 @@ __global__ __launch_bounds__(256) void k_expert_load(const uint8_t* __restrict__
 }
 
 // Row table: pair p = t*k + j goes to row bounds[e] + prefix[e][t/32] + (tokens
-// of word t/32 before t routed to e) -- stable in p.
+// of word t/32 before t routed to e) -- stable in p.  Every workgroup first
+// scans the E counts (E <= 1024: four per thread) into the group bounds in LDS;
+// workgroup 0 also writes the bounds and the GEMM row-tile list (expert, first
+// row, end row; kBM rows per tile; expert order) for the kernels that follow,
+// one tile per thread (its expert found by binary search over the experts'
+// first tiles: empty experts own no tiles).
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eidx, int64_t R, int k,
                                                  const uint32_t* __restrict__ mask,
                                                  const int32_t* __restrict__ wprefix,
-                                                 const int32_t* __restrict__ bounds, int W,
+                                                 const int32_t* __restrict__ counts, int E, int W,
+                                                 int32_t* __restrict__ bounds,
+                                                 int32_t* __restrict__ tiles,
+                                                 int32_t* __restrict__ ntiles,
                                                  int32_t* __restrict__ rows, int32_t* __restrict__ pos,
                                                  int32_t* __restrict__ rtok)
 {
-    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    __shared__ int s_bounds[kRouteMaxE];
+    __shared__ int s_tfirst[kRouteMaxE + 1];              // first tile of each expert (writer)
+    __shared__ int s_wc[4], s_wt[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool writer = blockIdx.x == 0;
+    int c4[4], t4[4], sc = 0, st = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ee = tid * 4 + i;
+        c4[i] = ee < E ? counts[ee] : 0;
+        t4[i] = (c4[i] + kBM - 1) / kBM;
+        sc += c4[i];
+        st += t4[i];
+    }
+    int ic = sc, it = st;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int yc = __shfl_up(ic, o);
+        const int yt = __shfl_up(it, o);
+        if (lane >= o) {
+            ic += yc;
+            it += yt;
+        }
+    }
+    if (lane == 63) {
+        s_wc[wave] = ic;
+        s_wt[wave] = it;
+    }
+    __syncthreads();
+    int bc = 0, bt = 0, all_c = 0, all_t = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bc += i < wave ? s_wc[i] : 0;
+        bt += i < wave ? s_wt[i] : 0;
+        all_c += s_wc[i];
+        all_t += s_wt[i];
+    }
+    int start = bc + ic - sc, tstart = bt + it - st;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ee = tid * 4 + i;
+        if (ee < E) {
+            s_bounds[ee] = start;
+            s_tfirst[ee] = tstart;
+            if (writer) bounds[ee] = start;
+        }
+        start += c4[i];
+        tstart += t4[i];
+    }
+    if (tid == 0) s_tfirst[E] = all_t;
+    if (writer && tid == 0) {
+        bounds[E] = all_c;
+        *ntiles = all_t;
+    }
+    __syncthreads();
+    if (writer) {
+        // tile tau belongs to the expert e with s_tfirst[e] <= tau < s_tfirst[e + 1]
+        for (int tau = tid; tau < all_t; tau += 256) {
+            int lo = 0, hi = E - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_tfirst[mid] <= tau)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            const int r0 = s_bounds[lo] + (tau - s_tfirst[lo]) * kBM;
+            const int rend = lo + 1 < E ? s_bounds[lo + 1] : all_c;
+            tiles[3 * tau + 0] = lo;
+            tiles[3 * tau + 1] = r0;
+            tiles[3 * tau + 2] = r0 + kBM < rend ? r0 + kBM : rend;
+        }
+    }
+    const int64_t p = (int64_t)blockIdx.x * 256 + tid;
     if (p >= R) return;
     const int t = (int)(p / k);
-    const int e = eidx[p];
+    int e = eidx[p];
+    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
     const int64_t wi = (int64_t)e * W + (t >> 5);
     const uint32_t below = mask[wi] & ((1u << (t & 31)) - 1u);
-    int row = bounds[e] + wprefix[wi] + __popc(below);
+    int row = s_bounds[e] + wprefix[wi] + __popc(below);
     // a consistent table always gives row in [0, R); the clamp only keeps an
     // inconsistent one from writing outside the buffers
     row = row < 0 ? 0 : (row >= (int)R ? (int)R - 1 : row);
@@ -756,15 +766,16 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
                        L.logits, L.T, L.E, L.k, L.eidx, L.wts, L.mask, L.W, n_route, L.x, xblocks,
                        L.d / 32, scale_stride(L.d), L.xq, L.dx);
     mark(L, kGroup, st);
-    hipLaunchKernelGGL(k_group, dim3(L.E), dim3(kGroupThreads), 0, st, L.mask, L.W, L.E, L.wprefix,
-                       L.counts, L.bounds, L.tiles, L.ntiles, L.done);
+    hipLaunchKernelGGL(k_group, dim3(L.E), dim3(kGroupThreads), 0, st, L.mask, L.W, L.wprefix,
+                       L.counts);
     mark(L, kExpertLoad, st);
     if (L.load_src)
         hipLaunchKernelGGL(k_expert_load, dim3(512), dim3(256), 0, st, L.load_src, L.load_dst, L.counts,
                            L.E, L.expert_stride, L.load_stats);
     mark(L, kScatter, st);
     hipLaunchKernelGGL(k_scatter, dim3(nblk(R, 256)), dim3(256), 0, st, L.eidx, R, L.k, L.mask,
-                       L.wprefix, L.bounds, L.W, L.rows, L.pos, L.rtok);
+                       L.wprefix, L.counts, L.E, L.W, L.bounds, L.tiles, L.ntiles, L.rows, L.pos,
+                       L.rtok);
     const int max_tiles_now = (int)((R + kBM - 1) / kBM) + (L.E < R ? L.E : (int)R);
 
     GemmArgs gu;

@@ -76,7 +76,7 @@ MOE_HD static inline int gu_logical_row(int nt, int j, int f)
 
 // -------------------------------------------------------------- workspace ---
 struct WsLayout {
-    uint64_t eidx, wts, mask, wprefix, counts, bounds, tiles, ntiles, done, load_stats;
+    uint64_t eidx, wts, mask, wprefix, counts, bounds, tiles, ntiles, load_stats;
     uint64_t rows, pos, rtok, xq, dx, gu, hq, dh, dm;
     uint64_t total;
     int W;            // 32-token words per expert in the membership mask
@@ -99,7 +99,6 @@ static inline WsLayout ws_layout(int d, int f, int E, int k, int Tmax)
     L.bounds = take((uint64_t)(E + 1) * 4);
     L.tiles = take((uint64_t)L.max_tiles * 3 * 4);
     L.ntiles = take(4);
-    L.done = take(4);
     L.load_stats = take(16);                              // experts, bytes of active-expert loads
     L.rows = take(R * 4);
     L.pos = take(R * 4);

@@ -372,7 +372,6 @@ int moe_prefill_create(const moe_prefill_params_t* pin, moe_prefill_t** out)
     }
     e = hipStreamCreateWithFlags(&h->copy, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipMemset(h->ws + h->L.mask, 0, (size_t)h->E * h->L.W * 4);
-    if (e == hipSuccess) e = hipMemset(h->ws + h->L.done, 0, 4);
     if (e == hipSuccess) e = hipMemset(h->ws + h->L.load_stats, 0, 16);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
@@ -460,7 +459,6 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
 
     if (h->mask_dirty) {   // a launch failed part-way: restore the grouping state first
         e = launch_fill_u32(reinterpret_cast<uint32_t*>(h->ws + h->L.mask), (int64_t)h->E * h->L.W, 0u, st);
-        if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(h->ws + h->L.done), 1, 0u, st);
         if (e != hipSuccess) return hip_fail(h, e, "grouping state reset");
         h->mask_dirty = false;
     }
@@ -496,7 +494,6 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
     LL.rows = reinterpret_cast<int32_t*>(w + h->L.rows);
     LL.pos = reinterpret_cast<int32_t*>(w + h->L.pos);
     LL.rtok = reinterpret_cast<int32_t*>(w + h->L.rtok);
-    LL.done = reinterpret_cast<uint32_t*>(w + h->L.done);
     LL.xq = reinterpret_cast<int8_t*>(w + h->L.xq);
     LL.dx = reinterpret_cast<float*>(w + h->L.dx);
     LL.gu = reinterpret_cast<float*>(w + h->L.gu);
