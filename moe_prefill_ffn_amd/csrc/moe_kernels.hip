@@ -98,15 +98,21 @@ __device__ __forceinline__ uint32_t q8_block_of8(float4 v, float* scale)
 // One launch, two kinds of workgroup.  Workgroups [0, n_route) route 4 tokens
 // each (one wave per token); the rest quantise X to Q8.
 //
-// Routing: the rank of logit e among the token's E logits is the number of
-// logits that beat it -- larger value, or equal value and lower index.  With
-// key(e) = (order-preserving bits of the logit, with -0 read as +0) << 32 |
-// (2^32 - 1 - e), "beats" is one unsigned 64-bit compare, so every lane ranks
-// its own logits against all E keys broadcast from LDS.  The logit of rank
-// j < k is slot j.  Router weights: softmax over the k selected logits, summed
-// in ascending slot order.  Each selected (token, expert) also sets the token's
-// bit in the expert membership mask read by the grouping step.
+// Routing: with key(e) = (order-preserving bits of the logit, with -0 read as
+// +0) << 32 | (2^32 - 1 - e), the order (larger logit first, ties to the lower
+// expert index) is the unsigned order of the 64-bit keys, and all keys differ.
+// Slot j of a token is the expert whose key has rank j.  Up to 128 experts the
+// ranks are counted directly (every lane compares its keys with all E keys,
+// broadcast from LDS); above that, each lane keeps the keys of experts lane,
+// lane + 64, ... in registers and slot j is the wave-wide maximum key after
+// slots 0 .. j-1 were taken out (k rounds of a lane-local maximum and a 6-step
+// butterfly): O(E k) instead of O(E^2) compares.  Both give the same slots.
+// Router weights: softmax over the k selected logits, summed in ascending slot
+// order.  Each selected (token, expert) also sets the token's bit in the expert
+// membership mask read by the grouping step.
 constexpr int kRouteMaxE = 1024;
+constexpr int kRouteKeys = kRouteMaxE / 64;     // keys per lane
+constexpr int kRankMaxE = 128;                  // rank counting up to this many experts
 
 __device__ __forceinline__ uint64_t route_key(float v, int e)
 {
@@ -115,10 +121,36 @@ __device__ __forceinline__ uint64_t route_key(float v, int e)
     return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
-__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
-                                            int32_t* __restrict__ eidx, float* __restrict__ wts,
-                                            uint32_t* __restrict__ mask, int W, uint64_t* keys,
-                                            float* zsel)
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
+{
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// router weights of the token's k slots, whose logits are in zsel[0 .. k)
+__device__ __forceinline__ void route_weights(int t, int k, float* __restrict__ wts, float* zsel)
+{
+    const int lane = threadIdx.x & 63;
+    __builtin_amdgcn_wave_barrier();
+    const float top = zsel[0];
+    const float z = lane < k ? exp_cw(zsel[lane] - top) : 0.0f;
+    __builtin_amdgcn_wave_barrier();
+    if (lane < k) zsel[lane] = z;
+    __builtin_amdgcn_wave_barrier();
+    float sum = 0.0f;
+    for (int j = 0; j < k; ++j) sum += zsel[j];
+    if (lane < k) wts[(int64_t)t * k + lane] = z / sum;
+}
+
+// E <= kRankMaxE: ranks counted against all keys (keys: this wave's LDS area)
+__device__ __forceinline__ void route_token_rank(const float* __restrict__ logits, int t, int E,
+                                                 int k, int32_t* __restrict__ eidx,
+                                                 float* __restrict__ wts,
+                                                 uint32_t* __restrict__ mask, int W,
+                                                 uint64_t* keys, float* zsel)
 {
     const int lane = threadIdx.x & 63;
     const float* lt = logits + (int64_t)t * E;
@@ -134,15 +166,38 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
             atomicOr(&mask[(int64_t)e * W + (t >> 5)], 1u << (t & 31));
         }
     }
-    __builtin_amdgcn_wave_barrier();
-    const float top = zsel[0];
-    const float z = lane < k ? exp_cw(zsel[lane] - top) : 0.0f;
-    __builtin_amdgcn_wave_barrier();
-    if (lane < k) zsel[lane] = z;
-    __builtin_amdgcn_wave_barrier();
-    float sum = 0.0f;
-    for (int j = 0; j < k; ++j) sum += zsel[j];
-    if (lane < k) wts[(int64_t)t * k + lane] = z / sum;
+    route_weights(t, k, wts, zsel);
+}
+
+template <int NK>   // keys per lane: E <= 64 * NK
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
+                                            int32_t* __restrict__ eidx, float* __restrict__ wts,
+                                            uint32_t* __restrict__ mask, int W, float* zsel)
+{
+    const int lane = threadIdx.x & 63;
+    const float* lt = logits + (int64_t)t * E;
+    uint64_t key[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = e < E ? route_key(lt[e], e) : 0ull;   // 0: below every real key
+    }
+    for (int j = 0; j < k; ++j) {
+        uint64_t m = key[0];
+#pragma unroll
+        for (int i = 1; i < NK; ++i) m = max_u64(m, key[i]);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) m = max_u64(m, shfl_xor_u64(m, o));
+        const int e = (int)(0xFFFFFFFFu - (uint32_t)m);  // the same on every lane
+#pragma unroll
+        for (int i = 0; i < NK; ++i) key[i] = key[i] == m ? 0ull : key[i];
+        if (lane == 0) {
+            eidx[(int64_t)t * k + j] = e;
+            zsel[j] = lt[e];
+            atomicOr(&mask[(int64_t)e * W + (t >> 5)], 1u << (t & 31));
+        }
+    }
+    route_weights(t, k, wts, zsel);
 }
 
 // x is a flat array of n_blocks 32-float blocks (a row-major [rows, K] matrix
@@ -171,12 +226,18 @@ __global__ __launch_bounds__(256) void k_route_quant(const float* __restrict__ l
                                                      int64_t n_blocks, int nbk, int dx_stride,
                                                      int8_t* __restrict__ xq, float* __restrict__ dx)
 {
-    __shared__ uint64_t keys[4][kRouteMaxE];
+    __shared__ uint64_t keys[4][kRankMaxE];
     __shared__ float zsel[4][64];
     if ((int)blockIdx.x < n_route) {
         const int wave = threadIdx.x >> 6;
         const int t = blockIdx.x * 4 + wave;
-        if (t < T) route_token(logits, t, E, k, eidx, wts, mask, W, keys[wave], zsel[wave]);
+        if (t >= T) return;
+        if (E <= kRankMaxE)
+            route_token_rank(logits, t, E, k, eidx, wts, mask, W, keys[wave], zsel[wave]);
+        else if (E <= 256)
+            route_token<4>(logits, t, E, k, eidx, wts, mask, W, zsel[wave]);
+        else
+            route_token<kRouteKeys>(logits, t, E, k, eidx, wts, mask, W, zsel[wave]);
         return;
     }
     const int64_t g = (int64_t)(blockIdx.x - n_route) * 256 + threadIdx.x;

@@ -50,6 +50,8 @@ def test_resident_real_shape_all_stages():
     (64, 128, 128, 1, 1, None),         # exactly one full 64-row tile
     (300, 256, 256, 64, 4, ("zipf", 1.1)),   # many empty experts
     (129, 192, 320, 5, 5, None),        # k = E: every expert gets every token
+    (70, 64, 64, 257, 8, None),         # E > 256: 16 routing keys per lane
+    (40, 64, 64, 1024, 12, None),       # the largest E
 ])
 def test_edge_shapes(T, d, f, E, k, bias):
     w = wl.small_workload(T, d, f, E, k, seed_base=77 + T + E, bias=bias)
@@ -126,6 +128,23 @@ def test_tied_logits_pick_lowest_experts():
     check_full_parity(w, g, ref)
     assert np.array_equal(g["eidx"][1], [0, 1, 2, 3])
     assert np.array_equal(g["eidx"][0], [7, 0, 1, 2])
+
+
+@pytest.mark.parametrize("E", [100, 200])
+def test_tied_logits_both_routing_methods(E):
+    """Ties (equal logits, -0 against +0) resolve to the lower expert index both
+    where ranks are counted (E <= 128) and where slots are taken by repeated
+    wave maxima (E > 128)."""
+    w = wl.small_workload(36, 64, 64, E, 6, seed_base=11 + E)
+    lg = np.zeros((w.T, w.E), np.float32)
+    lg[::2, E - 1] = 1.0                   # even tokens: the last expert first, then 0, 1, ...
+    lg[1::3, 5] = -0.0
+    lg[2::5, [E // 2, E // 3]] = 0.5       # two equal logits above the zeros
+    g, ref = _full_case(w, lg=lg)
+    check_full_parity(w, g, ref)
+    assert np.array_equal(g["eidx"][1], [0, 1, 2, 3, 4, 5])
+    assert np.array_equal(g["eidx"][0], [E - 1, 0, 1, 2, 3, 4])
+    assert np.array_equal(g["eidx"][7], [E // 3, E // 2, 0, 1, 2, 3])
 
 
 def test_zero_activations_give_zero_output():
