@@ -57,7 +57,7 @@ enum {
     MOE_EINVAL = -1,        /* bad argument, dimension or struct */
     MOE_ENOMEM = -2,        /* workspace or the mandatory pool slot not allocatable */
     MOE_EHIP = -3,          /* a HIP runtime call failed */
-    MOE_EUNSUPPORTED = -4,  /* device is not gfx950 */
+    MOE_EUNSUPPORTED = -4,  /* device is not gfx950, or lacks a feature the call needs */
     MOE_ESTATE = -5,        /* call not valid in the handle's state (e.g. layer >= 0 before a pool) */
     MOE_ETIMEOUT = -6       /* a bounded host wait expired */
 };
@@ -181,7 +181,7 @@ typedef struct stream_pool_params {
     int64_t max_vram_bytes;          /* > 0: budget for the pool; 0: no cap */
     int32_t requested_slots;         /* > 0: cap on the slot count; 0: derive */
     /* outputs */
-    int32_t eff_slots;               /* slots allocated (one contiguous allocation) */
+    int32_t eff_slots;               /* slots allocated (one device address range) */
     int32_t eff_depth;               /* effective prefetch depth */
     int32_t eff_residents;           /* resident leading layers */
     int32_t warnings;                /* MOE_WARN_* bits */
@@ -191,6 +191,11 @@ typedef struct stream_pool_params {
                                         loaded after its routing, only the experts that
                                         received rows; no lookahead prefetch (eff_depth 0) */
     int32_t reserved1;
+    int64_t reserve_bytes;           /* > 0: device memory to keep free.  When a pass starts
+                                        (moe_prefill_run_layer with layer 0) and the device
+                                        has less free memory than this, the pool shrinks by
+                                        the difference as stream_pool_set_budget does.
+                                        0: off */
 } stream_pool_params_t;
 
 #define MOE_WARN_SLOT_OVER_BUDGET 1  /* the one mandatory slot exceeds max_vram_bytes */
@@ -203,9 +208,11 @@ typedef struct stream_pool_params {
  *  - one slot is mandatory execution memory, tried even above the budget
  *    (warning); the prefetch window is served before optional residents;
  *    only residents + 1 + depth slots are allocated, never the whole budget;
- *  - the pool is one contiguous device allocation of fixed-size slots; on
- *    allocation failure fewer slots of the same size are tried (residents
- *    first, then depth) down to one; if one slot fails: MOE_ENOMEM;
+ *  - the pool is one contiguous device address range of fixed-size slots
+ *    (each slot its own physical allocation where the device has virtual
+ *    memory management, else one allocation); on allocation failure fewer
+ *    slots of the same size are tried (residents first, then depth) down to
+ *    one; if one slot fails: MOE_ENOMEM;
  *  - resident layers are uploaded before returning;
  *  - active_only (the survey's "active-expert-only streaming"): the layer's
  *    routing decides its copy.  After the grouping step of moe_prefill_run_layer
@@ -220,6 +227,40 @@ typedef struct stream_pool_params {
  * Effective values are written back into *inout.
  */
 int stream_pool_configure(moe_prefill_t* h, stream_pool_params_t* inout);
+
+/* Memory pressure (page #1905 "Summary": residents are evicted from the end of
+ * the resident prefix when memory runs short, and the active segment never).
+ * Shrinks the configured pool to at most max_vram_bytes (> 0) of slots and
+ * returns the freed device memory at once:
+ *  - resident layers leave from the end of the resident prefix first and are
+ *    streamed from then on; a pool without a streaming slot keeps the first
+ *    evicted layer's slot (and its data) as its streaming slot;
+ *  - then prefetch slots (the effective depth drops), never below one slot:
+ *    that slot is execution memory and stays even above the budget
+ *    (MOE_WARN_SLOT_OVER_BUDGET);
+ *  - a slot is released only after the work queued on it (its last layer's
+ *    kernels, a copy into it) has finished: a bounded host wait
+ *    (MOE_ETIMEOUT when it expires);
+ *  - the pool is one reserved device address range whose slots each have
+ *    their own physical allocation (HIP virtual memory), so released slots
+ *    return their memory without moving the others.  A device without
+ *    virtual memory management gets a single allocation at configure time and
+ *    MOE_EUNSUPPORTED here.
+ * Later passes produce the same outputs, with more layers streamed.  The
+ * budget only shrinks the pool; stream_pool_configure builds a larger one. */
+typedef struct stream_pool_budget {
+    uint32_t struct_size;
+    int32_t reserved0;
+    int64_t max_vram_bytes;          /* in: the new pool budget, > 0 */
+    /* outputs */
+    int32_t eff_slots;               /* slots still holding memory */
+    int32_t eff_depth;               /* effective prefetch depth */
+    int32_t eff_residents;           /* resident leading layers */
+    int32_t warnings;                /* MOE_WARN_* bits */
+    uint64_t released_bytes;         /* device memory returned by this call */
+} stream_pool_budget_t;
+
+int stream_pool_set_budget(moe_prefill_t* h, stream_pool_budget_t* inout);
 
 /* Pure planning step of stream_pool_configure (no device, no allocation), for
  * callers that want to see the plan first.  max_alloc_slots simulates the
@@ -240,6 +281,25 @@ typedef struct moe_pool_plan {
 
 int moe_prefill_plan_pool(moe_pool_plan_t* inout);
 
+/* Pure planning step of stream_pool_set_budget: which slots a live pool of
+ * `residents` resident and `streaming` streaming slots (an n_layers stack)
+ * gives up to fit budget_slots slots.  No device, no allocation. */
+typedef struct moe_pool_trim {
+    uint32_t struct_size;
+    int32_t n_layers;
+    int32_t residents;               /* in: resident slots now */
+    int32_t streaming;               /* in: streaming slots now */
+    int64_t budget_slots;            /* in: slots the budget holds (may be 0) */
+    /* outputs */
+    int32_t new_residents, new_streaming;
+    int32_t evicted;                 /* residents evicted, from the end of the prefix */
+    int32_t converted;               /* 1: the first evicted resident's slot became the streaming slot */
+    int32_t released;                /* slots whose memory is returned */
+    int32_t warnings;                /* MOE_WARN_* bits */
+} moe_pool_trim_t;
+
+int moe_prefill_plan_trim(moe_pool_trim_t* inout);
+
 /* ---------------------------------------------------------------- stats --- */
 
 typedef struct moe_stats {
@@ -256,6 +316,9 @@ typedef struct moe_stats {
     uint64_t sparse_loads;           /* active-expert loads launched */
     uint64_t experts_loaded;         /* experts those loads copied (device-counted) */
     uint64_t bytes_sparse;           /* bytes they copied (device-counted) */
+    uint64_t evicted_residents;      /* resident layers given up under memory pressure */
+    uint64_t released_bytes;         /* device memory the pool returned under pressure */
+    uint64_t pressure_trims;         /* shrinks started by reserve_bytes at a pass start */
 } moe_stats_t;
 
 /* Counters of the handle.  experts_loaded and bytes_sparse are kept on the

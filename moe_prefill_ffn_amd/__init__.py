@@ -57,7 +57,19 @@ class stream_pool_params_t(ctypes.Structure):
                 ("layer_bytes", _u64), ("prefetch_depth", _i32), ("resident_layers", _i32),
                 ("max_vram_bytes", _i64), ("requested_slots", _i32), ("eff_slots", _i32),
                 ("eff_depth", _i32), ("eff_residents", _i32), ("warnings", _i32), ("reserved0", _i32),
-                ("active_only", _i32), ("reserved1", _i32)]
+                ("active_only", _i32), ("reserved1", _i32), ("reserve_bytes", _i64)]
+
+
+class stream_pool_budget_t(ctypes.Structure):
+    _fields_ = [("struct_size", _u32), ("reserved0", _i32), ("max_vram_bytes", _i64),
+                ("eff_slots", _i32), ("eff_depth", _i32), ("eff_residents", _i32), ("warnings", _i32),
+                ("released_bytes", _u64)]
+
+
+class moe_pool_trim_t(ctypes.Structure):
+    _fields_ = [("struct_size", _u32), ("n_layers", _i32), ("residents", _i32), ("streaming", _i32),
+                ("budget_slots", _i64), ("new_residents", _i32), ("new_streaming", _i32),
+                ("evicted", _i32), ("converted", _i32), ("released", _i32), ("warnings", _i32)]
 
 
 class moe_pool_plan_t(ctypes.Structure):
@@ -72,7 +84,8 @@ class moe_stats_t(ctypes.Structure):
                 ("prefetch_queued", _u64), ("prefetch_activated", _u64), ("sync_loads", _u64),
                 ("prefetch_failed", _u64), ("bytes_h2d", _u64), ("eff_slots", _i32),
                 ("eff_depth", _i32), ("eff_residents", _i32), ("warnings", _i32),
-                ("sparse_loads", _u64), ("experts_loaded", _u64), ("bytes_sparse", _u64)]
+                ("sparse_loads", _u64), ("experts_loaded", _u64), ("bytes_sparse", _u64),
+                ("evicted_residents", _u64), ("released_bytes", _u64), ("pressure_trims", _u64)]
 
 
 MOE_N_KERNELS = 7
@@ -87,7 +100,8 @@ EXPORTED_SYMBOLS = [
     "moe_prefill_workspace_size", "moe_prefill_create", "moe_prefill_destroy",
     "moe_prefill_last_error", "moe_prefill_expert_bytes", "moe_prefill_layer_bytes",
     "moe_prefill_pack_expert", "moe_prefill_run_layer", "stream_pool_configure",
-    "moe_prefill_plan_pool", "moe_prefill_get_stats", "moe_prefill_set_timing",
+    "moe_prefill_plan_pool", "moe_prefill_plan_trim", "stream_pool_set_budget",
+    "moe_prefill_get_stats", "moe_prefill_set_timing",
     "moe_prefill_kernel_times", "moe_prefill_kernel_name",
 ]
 
@@ -117,6 +131,8 @@ def lib():
     L.moe_prefill_run_layer.argtypes = [_vp, ctypes.POINTER(moe_layer_io_t), _vp]
     L.stream_pool_configure.argtypes = [_vp, ctypes.POINTER(stream_pool_params_t)]
     L.moe_prefill_plan_pool.argtypes = [ctypes.POINTER(moe_pool_plan_t)]
+    L.moe_prefill_plan_trim.argtypes = [ctypes.POINTER(moe_pool_trim_t)]
+    L.stream_pool_set_budget.argtypes = [_vp, ctypes.POINTER(stream_pool_budget_t)]
     L.moe_prefill_get_stats.argtypes = [_vp, ctypes.POINTER(moe_stats_t)]
     L.moe_prefill_set_timing.argtypes = [_vp, _i32]
     L.moe_prefill_kernel_times.argtypes = [_vp, ctypes.POINTER(moe_kernel_times_t), _i32]
@@ -300,9 +316,11 @@ def moe_prefill_run_layer(handle: Handle, x: torch.Tensor, logits: torch.Tensor,
 
 def stream_pool_configure(handle: Handle, host_blobs: Sequence[torch.Tensor], prefetch_depth: int = 1,
                           resident_layers: int = 0, max_vram_bytes: int = 0,
-                          requested_slots: int = 0, active_only: bool = False) -> dict:
+                          requested_slots: int = 0, active_only: bool = False,
+                          reserve_bytes: int = 0) -> dict:
     """Plan + allocate the slot pool over pinned host blobs (one per layer).
-    active_only: streamed layers are loaded after their routing, only the experts with rows."""
+    active_only: streamed layers are loaded after their routing, only the experts with rows.
+    reserve_bytes: device memory to keep free; checked when a pass starts (layer 0)."""
     p = stream_pool_params_t()
     p.struct_size = ctypes.sizeof(p)
     n = len(host_blobs)
@@ -321,9 +339,30 @@ def stream_pool_configure(handle: Handle, host_blobs: Sequence[torch.Tensor], pr
     p.max_vram_bytes = max_vram_bytes
     p.requested_slots = requested_slots
     p.active_only = 1 if active_only else 0
+    p.reserve_bytes = reserve_bytes
     _check(lib().stream_pool_configure(handle.ptr, ctypes.byref(p)), handle.ptr)
     handle._pool_keep = list(host_blobs)
     return dict(slots=p.eff_slots, depth=p.eff_depth, residents=p.eff_residents, warnings=p.warnings)
+
+
+def stream_pool_set_budget(handle: Handle, max_vram_bytes: int) -> dict:
+    """Shrink the live pool to max_vram_bytes (memory pressure); returns the effective shape
+    and the device bytes released."""
+    p = stream_pool_budget_t()
+    p.struct_size = ctypes.sizeof(p)
+    p.max_vram_bytes = max_vram_bytes
+    _check(lib().stream_pool_set_budget(handle.ptr, ctypes.byref(p)), handle.ptr)
+    return dict(slots=p.eff_slots, depth=p.eff_depth, residents=p.eff_residents, warnings=p.warnings,
+                released_bytes=p.released_bytes)
+
+
+def moe_prefill_plan_trim(n_layers: int, residents: int, streaming: int, budget_slots: int) -> dict:
+    p = moe_pool_trim_t()
+    p.struct_size = ctypes.sizeof(p)
+    p.n_layers, p.residents, p.streaming, p.budget_slots = n_layers, residents, streaming, budget_slots
+    rc = lib().moe_prefill_plan_trim(ctypes.byref(p))
+    return dict(rc=rc, residents=p.new_residents, streaming=p.new_streaming, evicted=p.evicted,
+                converted=p.converted, released=p.released, warnings=p.warnings)
 
 
 def moe_prefill_plan_pool(n_layers: int, slot_bytes: int, prefetch_depth: int, resident_layers: int,

@@ -10,7 +10,9 @@
 //    pool-behaviour table: only the peak slot count is allocated; the one
 //    mandatory slot is execution memory and is tried even above the budget
 //    (with a warning); on allocation failure progressively smaller pools of
-//    the same slot size are tried; if one slot fails, creation fails clearly.
+//    the same slot size are tried; if one slot fails, creation fails clearly;
+//  - #1905 "Summary": under runtime memory pressure residents are evicted from
+//    the end of the resident prefix (plan_trim), the active segment never.
 #include "moe_pool_plan.h"
 
 #include <stdint.h>
@@ -62,6 +64,38 @@ PoolShape plan_degrade(const PoolShape& cur, int L, int depth_req, int residents
     *warnings |= kWarnPoolDegraded;
     if (s.depth < depth_req && s.residents < L) *warnings |= kWarnDepthReduced;
     return s;
+}
+
+PoolTrim plan_trim(int L, int residents, int streaming, int64_t budget_slots, int* warnings)
+{
+    PoolTrim t;
+    t.residents = residents;
+    t.streaming = streaming;
+    int64_t alive = (int64_t)residents + streaming;
+    int64_t target = budget_slots;
+    if (target < 1) {
+        target = 1;
+        *warnings |= kWarnSlotOverBudget;
+    }
+    while (alive > target && t.residents > 0) {
+        --t.residents;
+        ++t.evicted;
+        if (t.streaming == 0) {
+            t.streaming = 1;       // the evicted layer's slot keeps it, now as a streaming slot
+            t.converted = 1;
+        } else {
+            ++t.released;
+            --alive;
+        }
+    }
+    const int depth_before = streaming > 0 ? streaming - 1 : 0;
+    while (alive > target && t.streaming > 1) {
+        --t.streaming;
+        ++t.released;
+        --alive;
+    }
+    if (t.residents < L && t.streaming - 1 < depth_before) *warnings |= kWarnDepthReduced;
+    return t;
 }
 
 }  // namespace moe

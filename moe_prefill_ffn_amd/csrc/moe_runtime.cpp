@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <array>
 #include <chrono>
 #include <string>
@@ -42,9 +43,19 @@ struct moe_prefill {
     bool active_only = false;
     std::vector<const uint8_t*> blobs_dev;   // device addresses of the pinned host blobs (active_only)
     uint64_t layer_bytes = 0, slot_bytes = 0;
-    PoolShape shape;
+    PoolShape shape;                 // the plan at configure time (shape.slots = address-range slots)
     int warnings = 0;
     uint8_t* pool = nullptr;
+    // pool memory: one reserved device address range.  With virtual memory management
+    // every slot has its own physical allocation, so a released slot returns its
+    // memory; otherwise the range is one hipMalloc and nothing is released early.
+    bool vmm = false;
+    uint64_t va_bytes = 0;
+    std::vector<hipMemGenericAllocationHandle_t> phys;
+    std::vector<char> slot_kind;     // kSlotStreaming / kSlotResident / kSlotReleased
+    int res_live = 0;                // resident leading layers now (layer i lives in slot i)
+    int depth_live = 0;              // effective prefetch depth now
+    int64_t reserve_bytes = 0;       // free device memory to keep (0: off)
     std::vector<int> slot_layer, layer_slot;
     std::vector<hipEvent_t> ev_ready, ev_free;
     std::vector<char> ready_set, free_set, from_prefetch;
@@ -194,12 +205,14 @@ bool dims_ok(const moe_prefill_params_t& p, std::string* why)
 
 // Layers of the prefetch window after `cur`: the next `depth` streamed layers
 // in pass order (wrapping to the next pass), never `cur` itself.
+enum : char { kSlotStreaming = 0, kSlotResident = 1, kSlotReleased = 2 };
+
 std::vector<int> window_after(const moe_prefill_t* h, int cur)
 {
     std::vector<int> w;
-    const int res = h->shape.residents;
+    const int res = h->res_live;
     if (res >= h->nl) return w;
-    for (int i = 1; i < h->nl && (int)w.size() < h->shape.depth; ++i) {
+    for (int i = 1; i < h->nl && (int)w.size() < h->depth_live; ++i) {
         const int y = (cur + i) % h->nl;
         if (y >= res && y != cur) w.push_back(y);
     }
@@ -213,8 +226,8 @@ int pick_victim(const moe_prefill_t* h, int cur, int exclude)
     const std::vector<int> win = window_after(h, cur);
     int best = -1;
     long best_score = -1;
-    for (int s = h->shape.residents; s < h->shape.slots; ++s) {
-        if (s == exclude) continue;
+    for (int s = 0; s < h->shape.slots; ++s) {
+        if (s == exclude || h->slot_kind[s] != kSlotStreaming) continue;
         const int lay = h->slot_layer[s];
         bool keep = lay >= 0 && lay == cur;
         for (int y : win) keep = keep || lay == y;
@@ -248,6 +261,164 @@ hipError_t enqueue_copy(moe_prefill_t* h, int s, int layer)
     return hipSuccess;
 }
 
+// Pool memory for n slots of slot_bytes: a reserved address range with one physical
+// allocation mapped per slot (vmm), else one hipMalloc.  On failure nothing is left allocated.
+hipError_t pool_alloc(moe_prefill_t* h, int n, uint64_t slot_bytes)
+{
+    const uint64_t bytes = (uint64_t)n * slot_bytes;
+    h->phys.assign(n, 0);
+    if (!h->vmm) {
+        h->va_bytes = bytes;
+        return hipMalloc(reinterpret_cast<void**>(&h->pool), bytes);
+    }
+    void* va = nullptr;
+    hipError_t e = hipMemAddressReserve(&va, bytes, 0, nullptr, 0);
+    if (e != hipSuccess) return e;
+    hipMemAllocationProp prop = {};
+    prop.type = hipMemAllocationTypePinned;
+    prop.location.type = hipMemLocationTypeDevice;
+    prop.location.id = h->dev;
+    hipMemAccessDesc acc = {};
+    acc.location = prop.location;
+    acc.flags = hipMemAccessFlagsProtReadWrite;
+    int mapped = 0;
+    for (; mapped < n && e == hipSuccess; ++mapped) {
+        char* at = static_cast<char*>(va) + (uint64_t)mapped * slot_bytes;
+        e = hipMemCreate(&h->phys[mapped], slot_bytes, &prop, 0);
+        if (e != hipSuccess) break;
+        e = hipMemMap(at, slot_bytes, 0, h->phys[mapped], 0);
+        if (e != hipSuccess) {
+            (void)hipMemRelease(h->phys[mapped]);
+            break;
+        }
+        e = hipMemSetAccess(at, slot_bytes, &acc, 1);
+        if (e != hipSuccess) {
+            (void)hipMemUnmap(at, slot_bytes);
+            (void)hipMemRelease(h->phys[mapped]);
+            break;
+        }
+    }
+    if (e != hipSuccess) {
+        for (int i = 0; i < mapped; ++i) {
+            (void)hipMemUnmap(static_cast<char*>(va) + (uint64_t)i * slot_bytes, slot_bytes);
+            (void)hipMemRelease(h->phys[i]);
+        }
+        (void)hipMemAddressFree(va, bytes);
+        h->phys.clear();
+        return e;
+    }
+    h->pool = static_cast<uint8_t*>(va);
+    h->va_bytes = bytes;
+    return hipSuccess;
+}
+
+// Return slot s's memory (vmm only); its queued work must have finished.
+hipError_t slot_unmap(moe_prefill_t* h, int s)
+{
+    hipError_t e = hipMemUnmap(h->pool + (uint64_t)s * h->slot_bytes, h->slot_bytes);
+    if (e == hipSuccess) e = hipMemRelease(h->phys[s]);
+    h->phys[s] = 0;
+    h->slot_kind[s] = kSlotReleased;
+    return e;
+}
+
+void pool_free_memory(moe_prefill_t* h)
+{
+    if (!h->pool) return;
+    if (h->vmm) {
+        for (size_t s = 0; s < h->phys.size(); ++s) {
+            if (!h->phys[s]) continue;
+            (void)hipMemUnmap(h->pool + (uint64_t)s * h->slot_bytes, h->slot_bytes);
+            (void)hipMemRelease(h->phys[s]);
+        }
+        (void)hipMemAddressFree(h->pool, h->va_bytes);
+    } else {
+        (void)hipFree(h->pool);
+    }
+    h->phys.clear();
+    h->pool = nullptr;
+    h->va_bytes = 0;
+}
+
+// Wait (bounded) for the work queued on slot s: its last layer's kernels and any copy into it.
+int slot_quiesce(moe_prefill_t* h, int s)
+{
+    if (h->free_set[s]) {
+        const int rc = wait_event(h, h->ev_free[s]);
+        if (rc != MOE_OK) return rc;
+    }
+    if (h->ready_set[s]) {
+        const int rc = wait_event(h, h->ev_ready[s]);
+        if (rc != MOE_OK) return rc;
+    }
+    return MOE_OK;
+}
+
+int count_slots(const moe_prefill_t* h, char kind)
+{
+    int n = 0;
+    for (char k : h->slot_kind) n += k == kind;
+    return n;
+}
+
+// Shrink the live pool to budget_bytes (memory pressure): residents leave from the end of
+// the resident prefix, then prefetch slots, never the last slot (plan_trim).
+int pool_trim(moe_prefill_t* h, int64_t budget_bytes, uint64_t* released, int* warn)
+{
+    const int n_stream = count_slots(h, kSlotStreaming);
+    const int64_t budget_slots = budget_bytes > 0 ? budget_bytes / (int64_t)h->slot_bytes : 0;
+    const PoolTrim t = plan_trim(h->nl, h->res_live, n_stream, budget_slots, warn);
+    for (int i = 0; i < t.evicted; ++i) {
+        const int r = h->res_live - 1;                    // layer r lives in slot r
+        int rc = slot_quiesce(h, r);
+        if (rc != MOE_OK) return rc;
+        if (t.converted && i == 0) {
+            h->slot_kind[r] = kSlotStreaming;             // keeps layer r, now as a streamed copy
+            h->from_prefetch[r] = 0;
+        } else {
+            h->layer_slot[r] = -1;
+            h->slot_layer[r] = -1;
+            const hipError_t e = slot_unmap(h, r);
+            if (e != hipSuccess) return hip_fail(h, e, "pool trim: release a resident slot");
+            *released += h->slot_bytes;
+        }
+        --h->res_live;
+        h->stats.evicted_residents++;
+    }
+    // prefetch slots: never the active one; empty slots first, then the layer needed last
+    for (int n = count_slots(h, kSlotStreaming); n > t.streaming; --n) {
+        int best = -1;
+        long best_score = -1;
+        for (int s = 0; s < h->shape.slots; ++s) {
+            if (h->slot_kind[s] != kSlotStreaming || s == h->active) continue;
+            const int lay = h->slot_layer[s];
+            const int cur = h->active >= 0 && h->slot_layer[h->active] >= 0 ? h->slot_layer[h->active] : 0;
+            const long score = lay < 0 ? (1L << 40) : (long)((lay - cur + h->nl) % h->nl);
+            if (score > best_score) {
+                best_score = score;
+                best = s;
+            }
+        }
+        if (best < 0) break;
+        int rc = slot_quiesce(h, best);
+        if (rc != MOE_OK) return rc;
+        if (h->slot_layer[best] >= 0) h->layer_slot[h->slot_layer[best]] = -1;
+        h->slot_layer[best] = -1;
+        const hipError_t e = slot_unmap(h, best);
+        if (e != hipSuccess) return hip_fail(h, e, "pool trim: release a prefetch slot");
+        *released += h->slot_bytes;
+    }
+    const int streaming = count_slots(h, kSlotStreaming);
+    h->depth_live = h->res_live < h->nl ? std::min(h->depth_live, streaming - 1) : 0;
+    if (h->depth_live < 0) h->depth_live = 0;
+    h->stats.released_bytes += *released;
+    h->stats.eff_slots = h->res_live + streaming;
+    h->stats.eff_depth = h->depth_live;
+    h->stats.eff_residents = h->res_live;
+    h->stats.warnings |= *warn;
+    return MOE_OK;
+}
+
 void pool_release(moe_prefill_t* h)
 {
     if (!h->pool_on && !h->pool) return;
@@ -256,8 +427,7 @@ void pool_release(moe_prefill_t* h)
         if (h->free_set[s]) (void)wait_event(h, h->ev_free[s]);
     for (hipEvent_t e : h->ev_ready) (void)hipEventDestroy(e);
     for (hipEvent_t e : h->ev_free) (void)hipEventDestroy(e);
-    if (h->pool) (void)hipFree(h->pool);
-    h->pool = nullptr;
+    pool_free_memory(h);
     h->pool_on = false;
     h->nl = 0;
     h->blobs.clear();
@@ -270,6 +440,9 @@ void pool_release(moe_prefill_t* h)
     h->ready_set.clear();
     h->free_set.clear();
     h->from_prefetch.clear();
+    h->slot_kind.clear();
+    h->res_live = h->depth_live = 0;
+    h->reserve_bytes = 0;
     h->active = -1;
     h->shape = PoolShape();
     h->warnings = 0;
@@ -427,9 +600,23 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
     } else {
         if (!h->pool_on) return fail(h, MOE_ESTATE, "layer >= 0 but no stream pool is configured");
         if (io.layer >= h->nl) return fail(h, MOE_ESTATE, "layer index beyond the configured stack");
+        if (io.layer == 0 && h->reserve_bytes > 0 && h->vmm) {
+            // a pass starts: give memory back if the device runs short of the reserve
+            size_t fr = 0, tot = 0;
+            if (hipMemGetInfo(&fr, &tot) == hipSuccess && (int64_t)fr < h->reserve_bytes) {
+                const int64_t live = (int64_t)(h->res_live + count_slots(h, kSlotStreaming)) * (int64_t)h->slot_bytes;
+                uint64_t rel = 0;
+                int w = 0;
+                const int rc = pool_trim(h, live - (h->reserve_bytes - (int64_t)fr), &rel, &w);
+                if (rc != MOE_OK) return rc;
+                h->stats.pressure_trims++;
+                h->warnings |= w;
+            }
+            (void)hipGetLastError();
+        }
         slot = h->layer_slot[io.layer];
         if (slot >= 0) {
-            if (slot >= h->shape.residents && h->ready_set[slot])
+            if (h->slot_kind[slot] == kSlotStreaming && h->ready_set[slot])
                 e = hipStreamWaitEvent(st, h->ev_ready[slot], 0);
             if (h->from_prefetch[slot]) {
                 h->stats.prefetch_activated++;
@@ -634,6 +821,26 @@ int moe_prefill_plan_pool(moe_pool_plan_t* inout)
     return MOE_OK;
 }
 
+int moe_prefill_plan_trim(moe_pool_trim_t* inout)
+{
+    moe_pool_trim_t p;
+    std::string why;
+    if (!read_struct(inout, &p, &why)) return fail(nullptr, MOE_EINVAL, why);
+    if (p.n_layers < 1 || p.residents < 0 || p.streaming < 0 || p.residents > p.n_layers ||
+        p.residents + p.streaming < 1 || (p.residents < p.n_layers && p.streaming < 1))
+        return fail(nullptr, MOE_EINVAL, "plan trim: not a pool the planner makes");
+    int warn = 0;
+    const PoolTrim t = plan_trim(p.n_layers, p.residents, p.streaming, p.budget_slots, &warn);
+    p.new_residents = t.residents;
+    p.new_streaming = t.streaming;
+    p.evicted = t.evicted;
+    p.converted = t.converted;
+    p.released = t.released;
+    p.warnings = warn;
+    write_struct(inout, p);
+    return MOE_OK;
+}
+
 int stream_pool_configure(moe_prefill_t* h, stream_pool_params_t* inout)
 {
     if (!h) return fail(nullptr, MOE_EINVAL, "null handle");
@@ -676,7 +883,25 @@ int stream_pool_configure(moe_prefill_t* h, stream_pool_params_t* inout)
             blobs_dev.push_back(dp);
         }
     }
-    const uint64_t slot_bytes = align_up(p.layer_bytes, 1 << 16);
+    int vmm = 0;
+    if (hipDeviceGetAttribute(&vmm, hipDeviceAttributeVirtualMemoryManagementSupported, h->dev) != hipSuccess) {
+        (void)hipGetLastError();
+        vmm = 0;
+    }
+    h->vmm = vmm != 0;
+    uint64_t align = 1 << 16;
+    if (h->vmm) {
+        hipMemAllocationProp prop = {};
+        prop.type = hipMemAllocationTypePinned;
+        prop.location.type = hipMemLocationTypeDevice;
+        prop.location.id = h->dev;
+        size_t gran = 0;
+        if (hipMemGetAllocationGranularity(&gran, &prop, hipMemAllocationGranularityRecommended) == hipSuccess &&
+            gran > align)
+            align = gran;
+        (void)hipGetLastError();
+    }
+    const uint64_t slot_bytes = align_up(p.layer_bytes, align);
     int warn = 0;
     const int want_depth = p.active_only ? 0 : p.prefetch_depth;   // routing decides the copy: no lookahead
     PoolShape s = plan_initial(p.n_layers, slot_bytes, want_depth, p.resident_layers,
@@ -684,14 +909,13 @@ int stream_pool_configure(moe_prefill_t* h, stream_pool_params_t* inout)
     const char* cap_env = getenv("MOE_TEST_POOL_MAX_SLOTS");
     const int cap = cap_env ? atoi(cap_env) : 0;
     const bool fail_all = getenv("MOE_TEST_POOL_FAIL_ALL") && atoi(getenv("MOE_TEST_POOL_FAIL_ALL"));
-    uint8_t* pool = nullptr;
     for (;;) {
         bool ok = !fail_all && !(cap > 0 && s.slots > cap);
         if (ok) {
-            const hipError_t e = hipMalloc(reinterpret_cast<void**>(&pool), (size_t)s.slots * slot_bytes);
+            const hipError_t e = pool_alloc(h, s.slots, slot_bytes);
             if (e != hipSuccess) {
                 (void)hipGetLastError();
-                pool = nullptr;
+                h->pool = nullptr;
                 ok = false;
             }
         }
@@ -704,7 +928,6 @@ int stream_pool_configure(moe_prefill_t* h, stream_pool_params_t* inout)
         s = plan_degrade(s, p.n_layers, want_depth, p.resident_layers, &warn);
     }
 
-    h->pool = pool;
     h->pool_on = true;
     h->nl = p.n_layers;
     h->blobs.assign(p.host_blobs, p.host_blobs + p.n_layers);
@@ -721,6 +944,11 @@ int stream_pool_configure(moe_prefill_t* h, stream_pool_params_t* inout)
     h->ready_set.assign(s.slots, 0);
     h->free_set.assign(s.slots, 0);
     h->from_prefetch.assign(s.slots, 0);
+    h->slot_kind.assign(s.slots, kSlotStreaming);
+    for (int i = 0; i < s.residents; ++i) h->slot_kind[i] = kSlotResident;
+    h->res_live = s.residents;
+    h->depth_live = s.depth;
+    h->reserve_bytes = p.reserve_bytes > 0 ? p.reserve_bytes : 0;
     h->active = -1;
     h->prefetch_counter = 0;
     const char* fa = getenv("MOE_TEST_PREFETCH_FAIL");
@@ -761,6 +989,33 @@ int stream_pool_configure(moe_prefill_t* h, stream_pool_params_t* inout)
     h->stats.eff_residents = s.residents;
     h->stats.warnings = warn;
     write_struct(inout, p);
+    h->err.clear();
+    return MOE_OK;
+}
+
+int stream_pool_set_budget(moe_prefill_t* h, stream_pool_budget_t* inout)
+{
+    if (!h) return fail(nullptr, MOE_EINVAL, "null handle");
+    stream_pool_budget_t p;
+    std::string why;
+    if (!read_struct(inout, &p, &why)) return fail(h, MOE_EINVAL, why);
+    if (!h->pool_on) return fail(h, MOE_ESTATE, "pool budget: no stream pool is configured");
+    if (p.max_vram_bytes <= 0) return fail(h, MOE_EINVAL, "pool budget: max_vram_bytes must be > 0");
+    if (!h->vmm)
+        return fail(h, MOE_EUNSUPPORTED, "pool budget: the device has no virtual memory management, "
+                                         "so the pool is one allocation; reconfigure it instead");
+    DevGuard guard(h->dev);
+    uint64_t rel = 0;
+    int w = 0;
+    const int rc = pool_trim(h, p.max_vram_bytes, &rel, &w);
+    h->warnings |= w;
+    p.eff_slots = h->res_live + count_slots(h, kSlotStreaming);
+    p.eff_depth = h->depth_live;
+    p.eff_residents = h->res_live;
+    p.warnings = w;
+    p.released_bytes = rel;
+    write_struct(inout, p);
+    if (rc != MOE_OK) return rc;
     h->err.clear();
     return MOE_OK;
 }

@@ -162,6 +162,51 @@ def test_plan_skewed_stack_three_slots():
 
 # ---------------------------------------------------- versioned structs ---
 
+def trim(L, residents, streaming, budget_slots):
+    return mp.moe_prefill_plan_trim(L, residents, streaming, budget_slots)
+
+
+def test_trim_evicts_from_the_end_of_the_resident_prefix_before_prefetch_slots():
+    # 48 layers, 4 residents + 3 streaming (depth 2): a 5-slot budget costs two residents
+    t = trim(48, 4, 3, 5)
+    assert (t["rc"], t["residents"], t["streaming"], t["evicted"], t["released"]) == (0, 2, 3, 2, 2)
+    assert t["converted"] == 0 and t["warnings"] == 0
+    # 3 slots: every resident goes, the prefetch window stays
+    t = trim(48, 4, 3, 3)
+    assert (t["residents"], t["streaming"], t["evicted"], t["released"]) == (0, 3, 4, 4)
+
+
+def test_trim_then_shrinks_the_prefetch_window():
+    t = trim(48, 4, 3, 2)
+    assert (t["residents"], t["streaming"], t["evicted"], t["released"]) == (0, 2, 4, 5)
+    assert t["warnings"] & mp.MOE_WARN_DEPTH_REDUCED
+
+
+def test_trim_keeps_one_slot_even_below_the_budget():
+    t = trim(8, 0, 3, 0)
+    assert (t["residents"], t["streaming"], t["released"]) == (0, 1, 2)
+    assert t["warnings"] & mp.MOE_WARN_SLOT_OVER_BUDGET
+
+
+def test_trim_of_an_all_resident_pool_keeps_a_streaming_slot():
+    # every layer resident (no streaming slot): the first evicted layer's slot becomes it
+    t = trim(4, 4, 0, 2)
+    assert (t["residents"], t["streaming"], t["evicted"], t["converted"], t["released"]) == (1, 1, 3, 1, 2)
+
+
+def test_trim_within_budget_changes_nothing():
+    t = trim(48, 4, 3, 7)
+    assert (t["residents"], t["streaming"], t["evicted"], t["released"], t["warnings"]) == (4, 3, 0, 0, 0)
+    t = trim(48, 4, 3, 100)
+    assert (t["residents"], t["streaming"], t["released"]) == (4, 3, 0)
+
+
+def test_trim_rejects_pools_the_planner_never_makes():
+    assert trim(4, 5, 1, 2)["rc"] == mp.MOE_EINVAL        # more residents than layers
+    assert trim(4, 2, 0, 2)["rc"] == mp.MOE_EINVAL        # streamed layers but no streaming slot
+    assert trim(4, 0, 0, 2)["rc"] == mp.MOE_EINVAL        # no slot at all
+
+
 def test_undersized_struct_takes_defaults():
     p = mp.moe_pool_plan_t()
     p.n_layers, p.slot_bytes, p.prefetch_depth, p.resident_layers = 4, S, 1, 0

@@ -243,3 +243,103 @@ def _raw_configure(h, blobs):
     p.layer_bytes = blobs[0].numel()
     p.active_only = 1
     mp._check(mp.lib().stream_pool_configure(h.ptr, ctypes.byref(p)), h.ptr)
+
+
+# ---------------------------------------------------------- memory pressure ---
+
+def _slot_bytes(st):
+    lb = st.blobs[0].numel()
+    return (lb + 65535) // 65536 * 65536
+
+
+def _passes_preallocated(st, h, passes, outs):
+    for p in range(passes):
+        for l in range(st.n):
+            mp.moe_prefill_run_layer(h, st.x[l], st.lg[l], outs[p][l], layer=l)
+    torch.cuda.synchronize()
+    for p in range(passes):
+        for l in range(st.n):
+            assert_equal(f"pass {p} layer {l}", outs[p][l].cpu().numpy(), st.ref[l])
+
+
+def test_budget_evicts_residents_from_the_end_and_returns_memory(tiny5):
+    h = make_handle(tiny5.w)
+    slot = _slot_bytes(tiny5)
+    plan = _configure(h, tiny5, prefetch_depth=1, resident_layers=-1, max_vram_bytes=5 * slot)
+    assert (plan["slots"], plan["depth"], plan["residents"]) == (5, 1, 3)
+    tiny5.check(tiny5.run_passes(h, 1))
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    b = mp.stream_pool_set_budget(h, 3 * slot)
+    free1 = torch.cuda.mem_get_info()[0]
+    assert (b["slots"], b["depth"], b["residents"], b["released_bytes"]) == (3, 1, 1, 2 * slot)
+    assert free1 - free0 >= 2 * slot - (1 << 20), (free0, free1)
+    tiny5.check(tiny5.run_passes(h, 2))
+    s = mp.moe_prefill_get_stats(h)
+    assert (s["eff_residents"], s["eff_slots"], s["evicted_residents"], s["released_bytes"]) == (1, 3, 2, 2 * slot)
+    assert s["prefetch_failed"] == 0
+    # the budget only shrinks: a larger one changes nothing
+    b = mp.stream_pool_set_budget(h, 10 * slot)
+    assert (b["slots"], b["residents"], b["released_bytes"]) == (3, 1, 0)
+    tiny5.check(tiny5.run_passes(h, 1))
+    h.close()
+
+
+def test_budget_on_an_all_resident_pool_keeps_a_streaming_slot(tiny5):
+    h = make_handle(tiny5.w)
+    slot = _slot_bytes(tiny5)
+    plan = _configure(h, tiny5, prefetch_depth=1, resident_layers=-1)
+    assert (plan["slots"], plan["depth"], plan["residents"]) == (5, 0, 5)
+    tiny5.check(tiny5.run_passes(h, 1))
+    b = mp.stream_pool_set_budget(h, 2 * slot)
+    assert (b["slots"], b["depth"], b["residents"], b["released_bytes"]) == (2, 0, 1, 3 * slot)
+    tiny5.check(tiny5.run_passes(h, 2))
+    s = mp.moe_prefill_get_stats(h)
+    assert s["evicted_residents"] == 4 and s["sync_loads"] > 0
+    h.close()
+
+
+def test_budget_below_one_slot_keeps_the_execution_slot(tiny5):
+    h = make_handle(tiny5.w)
+    slot = _slot_bytes(tiny5)
+    _configure(h, tiny5, prefetch_depth=2, resident_layers=0, requested_slots=3)
+    tiny5.check(tiny5.run_passes(h, 1))
+    b = mp.stream_pool_set_budget(h, 1)
+    assert (b["slots"], b["depth"], b["residents"], b["released_bytes"]) == (1, 0, 0, 2 * slot)
+    assert b["warnings"] & mp.MOE_WARN_SLOT_OVER_BUDGET and b["warnings"] & mp.MOE_WARN_DEPTH_REDUCED
+    tiny5.check(tiny5.run_passes(h, 2))
+    assert mp.moe_prefill_get_stats(h)["sync_loads"] >= 10
+    h.close()
+
+
+def test_budget_needs_a_pool_and_a_positive_budget(tiny5):
+    h = make_handle(tiny5.w)
+    with pytest.raises(mp.MoePrefillError) as e:
+        mp.stream_pool_set_budget(h, 1 << 30)
+    assert e.value.code == mp.MOE_ESTATE
+    _configure(h, tiny5, prefetch_depth=1, resident_layers=0, requested_slots=2)
+    with pytest.raises(mp.MoePrefillError) as e:
+        mp.stream_pool_set_budget(h, 0)
+    assert e.value.code == mp.MOE_EINVAL
+    h.close()
+
+
+def test_reserve_shrinks_the_pool_when_a_pass_starts(tiny5):
+    """Memory pressure from the host side: the reserve asks for more free device memory
+    than there is, so the next pass start gives residents back (from the end of the
+    prefix) until the shortfall is covered; later passes find the reserve met."""
+    w = tiny5.w
+    slot = _slot_bytes(tiny5)
+    outs = [[torch.empty(w.T, w.d, device="cuda") for _ in range(tiny5.n)] for _ in range(3)]
+    h = make_handle(w)
+    _configure(h, tiny5, prefetch_depth=1, resident_layers=-1, max_vram_bytes=5 * slot)
+    torch.cuda.synchronize()
+    free_now = torch.cuda.mem_get_info()[0]
+    plan = _configure(h, tiny5, prefetch_depth=1, resident_layers=-1, max_vram_bytes=5 * slot,
+                      reserve_bytes=free_now + slot + slot // 2)
+    assert plan["residents"] == 3
+    _passes_preallocated(tiny5, h, 3, outs)
+    s = mp.moe_prefill_get_stats(h)
+    assert s["pressure_trims"] == 1, s
+    assert (s["eff_residents"], s["evicted_residents"], s["released_bytes"]) == (1, 2, 2 * slot)
+    h.close()
