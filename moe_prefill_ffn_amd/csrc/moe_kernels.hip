@@ -662,6 +662,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
     // scale-area offsets: this lane's column scales, and the A scales of row = lane
     const int ws_off = wave * 1024 + j32 * 16;
     const int xs_off = (lane >> 4) * 1024 + 512 + (lane & 15) * 32;
+    const int xs_off1h = (j32 >> 4) * 1024 + 512 + (j32 & 15) * 32;   // row j32, for one row half
 
     // acc[i] += (float)is[i] * t[off + i] for the register groups that hold tile rows: element
     // i of a lane is row 8*(i/4) + 4*h + i%4 of its half, so group g = i/4 covers rows
@@ -694,6 +695,30 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
         const uint8_t* sb = ring + U * kStageBytes;
         const uint8_t* sc = sbuf + (grp & 1) * kScaleBytes;
         const uint4 bq = *reinterpret_cast<const uint4*>(sb + kB_OFF + wave * 1024 + lane * 16);
+        if (!kTwo) {
+            // one row half: a single scale MFMA serves both blocks of the stage (lanes
+            // 0-31 carry block 0's scales, lanes 32-63 block 1's, rows 0-31 either way):
+            // t[i] = block 0 products, t[16 + i] = block 1 products
+            const uint16_t hb = *reinterpret_cast<const uint16_t*>(sc + ws_off + U * 4 + h * 2);
+            const float dw = (float)__builtin_bit_cast(_Float16, hb);
+            const float dxv = *reinterpret_cast<const float*>(sc + xs_off1h + U * 8 + h * 4);
+            const v32f t = __builtin_amdgcn_mfma_f32_32x32x1f32(dxv, dw, fzero, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const uint32_t w0 = q ? bq.z : bq.x;
+                const uint32_t w1 = q ? bq.w : bq.y;
+                v4i bop;
+                bop.x = (int)nib_to_i8(w0 & 0x0F0F0F0Fu);
+                bop.y = (int)nib_to_i8((w0 >> 4) & 0x0F0F0F0Fu);
+                bop.z = (int)nib_to_i8(w1 & 0x0F0F0F0Fu);
+                bop.w = (int)nib_to_i8((w1 >> 4) & 0x0F0F0F0Fu);
+                const v4i a0 = *reinterpret_cast<const v4i*>(sb + kA_OFF + a_off0[q]);
+                const v16i is0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bop, zero, 0, 0, 0);
+                fma_groups(std::integral_constant<int, 0>{}, acc0, is0, t, 16 * q, G);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            return;
+        }
         const uint32_t bs = *reinterpret_cast<const uint32_t*>(sc + ws_off + U * 4);
         const float2 dx = *reinterpret_cast<const float2*>(sc + xs_off + (U >> 1) * 16 + (U & 1) * 8);
 #pragma unroll
@@ -718,8 +743,6 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
                 asm volatile("" : "+v"(is0) : "v"(is1));
                 fma_groups(std::integral_constant<int, 4>{}, acc0, is0, t, 0, G);
                 fma_groups(full_c, acc1, is1, t, 16, G);
-            } else {
-                fma_groups(std::integral_constant<int, 0>{}, acc0, is0, t, 0, G);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
