@@ -32,7 +32,9 @@
  *    passes; the library never frees caller memory.
  *  - `stream` arguments are a hipStream_t passed as void* (NULL = the null
  *    stream).  Work is enqueued on it and the call returns before completion;
- *    the library never calls hipDeviceSynchronize.
+ *    moe_prefill_run_layer and the pool calls never call hipDeviceSynchronize
+ *    (create does, once; moe_prefill_get_stats does when it reads device-side
+ *    counters).
  *  - A handle is not thread-safe; separate handles are independent.
  *  - Degradations (smaller pool, shallower prefetch, one slot above the
  *    budget, synchronous fallback) are warnings: the call succeeds and the
@@ -324,6 +326,25 @@ typedef struct moe_stats {
 /* Counters of the handle.  experts_loaded and bytes_sparse are kept on the
  * device; reading them waits for the device to finish its queued work. */
 int moe_prefill_get_stats(const moe_prefill_t* h, moe_stats_t* inout);
+
+/* ------------------------------------------------------------- logging --- */
+
+#define MOE_LOG_ERROR 0
+#define MOE_LOG_WARN 1
+#define MOE_LOG_INFO 2
+
+/* One message: its level (MOE_LOG_*), text (valid during the call) and the
+ * user pointer given to moe_prefill_set_log. */
+typedef void (*moe_log_fn)(int32_t level, const char* message, void* user);
+
+/* Log sink of the handle: failed calls (level ERROR), degradations (WARN: a
+ * smaller pool, a reduced prefetch depth, a slot above the budget, a prefetch
+ * that fell back to a synchronous load, memory-pressure evictions) and pool
+ * decisions (INFO) with level <= `level` go to fn.  fn == NULL removes the
+ * sink.  Without a sink, MOE_LOG_LEVEL=<n> in the environment prints messages
+ * of level <= n to stderr.  Host only; the callback runs on the calling
+ * thread inside the library call. */
+int moe_prefill_set_log(moe_prefill_t* h, moe_log_fn fn, void* user, int32_t level);
 
 /* ------------------------------------------------------------- tracing --- */
 

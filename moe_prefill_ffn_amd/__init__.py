@@ -89,6 +89,8 @@ class moe_stats_t(ctypes.Structure):
 
 
 MOE_N_KERNELS = 7
+MOE_LOG_ERROR, MOE_LOG_WARN, MOE_LOG_INFO = 0, 1, 2
+_LOG_FN = ctypes.CFUNCTYPE(None, _i32, ctypes.c_char_p, _vp)
 
 
 class moe_kernel_times_t(ctypes.Structure):
@@ -101,7 +103,7 @@ EXPORTED_SYMBOLS = [
     "moe_prefill_last_error", "moe_prefill_expert_bytes", "moe_prefill_layer_bytes",
     "moe_prefill_pack_expert", "moe_prefill_run_layer", "stream_pool_configure",
     "moe_prefill_plan_pool", "moe_prefill_plan_trim", "stream_pool_set_budget",
-    "moe_prefill_get_stats", "moe_prefill_set_timing",
+    "moe_prefill_get_stats", "moe_prefill_set_log", "moe_prefill_set_timing",
     "moe_prefill_kernel_times", "moe_prefill_kernel_name",
 ]
 
@@ -134,6 +136,7 @@ def lib():
     L.moe_prefill_plan_trim.argtypes = [ctypes.POINTER(moe_pool_trim_t)]
     L.stream_pool_set_budget.argtypes = [_vp, ctypes.POINTER(stream_pool_budget_t)]
     L.moe_prefill_get_stats.argtypes = [_vp, ctypes.POINTER(moe_stats_t)]
+    L.moe_prefill_set_log.argtypes = [_vp, _LOG_FN, _vp, _i32]
     L.moe_prefill_set_timing.argtypes = [_vp, _i32]
     L.moe_prefill_kernel_times.argtypes = [_vp, ctypes.POINTER(moe_kernel_times_t), _i32]
     L.moe_prefill_kernel_name.argtypes = [_i32]
@@ -162,6 +165,7 @@ class Handle:
         self.params = params
         self._keep = list(keep)
         self._pool_keep = []
+        self._log_cb = None
 
     def __del__(self):
         try:
@@ -382,6 +386,18 @@ def moe_prefill_get_stats(handle: Handle) -> dict:
     s.struct_size = ctypes.sizeof(s)
     _check(lib().moe_prefill_get_stats(handle.ptr, ctypes.byref(s)), handle.ptr)
     return {name: getattr(s, name) for name, _ in moe_stats_t._fields_ if name not in ("struct_size", "reserved0")}
+
+
+# --------------------------------------------------------------- logging ---
+
+def moe_prefill_set_log(handle: Handle, fn: Optional[Callable[[int, str], None]], level: int = MOE_LOG_WARN) -> None:
+    """Route the handle's messages of level <= `level` to fn(level, text); fn=None removes the sink."""
+    if fn is None:
+        cb = ctypes.cast(None, _LOG_FN)
+    else:
+        cb = _LOG_FN(lambda lv, msg, user: fn(int(lv), msg.decode(errors="replace")))
+    handle._log_cb = cb                    # the library keeps the pointer: keep the callback alive
+    _check(lib().moe_prefill_set_log(handle.ptr, cb, None, level), handle.ptr)
 
 
 # --------------------------------------------------------------- tracing ---

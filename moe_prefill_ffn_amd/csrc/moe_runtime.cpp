@@ -3,6 +3,7 @@
 // HIP stream, event fencing, stats and errors.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -65,6 +66,12 @@ struct moe_prefill {
 
     moe_stats_t stats{};
 
+    // logging
+    moe_log_fn log_fn = nullptr;
+    void* log_user = nullptr;
+    int log_level = -1;               // sink threshold; -1: MOE_LOG_LEVEL decides (stderr)
+    bool poison = false;              // MOE_DEBUG_POISON: fill a slot with NaN bytes before each refill
+
     // kernel timing
     bool timing = false;
     struct TimedLayer {
@@ -79,13 +86,40 @@ struct moe_prefill {
 
 static thread_local std::string g_err;
 
+static int env_log_level()
+{
+    const char* e = getenv("MOE_LOG_LEVEL");
+    return e ? atoi(e) : -1;
+}
+
+static void log_msg(const moe_prefill_t* h, int level, const std::string& msg)
+{
+    if (h && h->log_fn) {
+        if (level <= h->log_level) h->log_fn(level, msg.c_str(), h->log_user);
+        return;
+    }
+    if (level <= env_log_level()) {
+        static const char* tag[3] = {"error", "warning", "info"};
+        fprintf(stderr, "moe_prefill %s: %s\n", tag[level < 0 ? 0 : (level > 2 ? 2 : level)], msg.c_str());
+    }
+}
+
 static int fail(moe_prefill_t* h, int code, const std::string& msg)
 {
     if (h)
         h->err = msg;
     else
         g_err = msg;
+    log_msg(h, MOE_LOG_ERROR, msg);
     return code;
+}
+
+// the MOE_WARN_* bits as one message (nothing if none is set)
+static void log_warnings(const moe_prefill_t* h, int warn, const std::string& where)
+{
+    if (warn & kWarnSlotOverBudget) log_msg(h, MOE_LOG_WARN, where + ": the one mandatory slot exceeds the budget");
+    if (warn & kWarnPoolDegraded) log_msg(h, MOE_LOG_WARN, where + ": allocation failed, a smaller pool is used");
+    if (warn & kWarnDepthReduced) log_msg(h, MOE_LOG_WARN, where + ": prefetch depth reduced to fit");
 }
 
 static int hip_fail(moe_prefill_t* h, hipError_t e, const char* what)
@@ -249,6 +283,9 @@ hipError_t enqueue_copy(moe_prefill_t* h, int s, int layer)
     h->from_prefetch[s] = 0;
     hipError_t e = hipSuccess;
     if (h->free_set[s]) e = hipStreamWaitEvent(h->copy, h->ev_free[s], 0);
+    if (e == hipSuccess && h->poison)   // debug: a read of the slot between free and refill sees NaN
+        e = launch_fill_u32(reinterpret_cast<uint32_t*>(h->pool + (uint64_t)s * h->slot_bytes),
+                            (int64_t)(h->slot_bytes / 4), 0xFFFFFFFFu, h->copy);
     if (e == hipSuccess)
         e = hipMemcpyAsync(h->pool + (uint64_t)s * h->slot_bytes, h->blobs[layer], h->layer_bytes,
                            hipMemcpyHostToDevice, h->copy);
@@ -611,6 +648,9 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
                 if (rc != MOE_OK) return rc;
                 h->stats.pressure_trims++;
                 h->warnings |= w;
+                log_msg(h, MOE_LOG_WARN, "device memory below the reserve: the pool released " +
+                        std::to_string(rel) + " bytes, " + std::to_string(h->res_live) + " residents left");
+                log_warnings(h, w, "memory pressure");
             }
             (void)hipGetLastError();
         }
@@ -630,6 +670,9 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
             if (old >= 0) h->layer_slot[old] = -1;
             h->slot_layer[slot] = -1;                     // a partial layer: never reused as whole
             if (h->free_set[slot]) e = hipStreamWaitEvent(st, h->ev_free[slot], 0);
+            if (e == hipSuccess && h->poison)   // debug: the experts that are not loaded hold NaN bytes
+                e = launch_fill_u32(reinterpret_cast<uint32_t*>(h->pool + (uint64_t)slot * h->slot_bytes),
+                                    (int64_t)(h->slot_bytes / 4), 0xFFFFFFFFu, st);
             sparse_slot = slot;
             h->stats.sparse_loads++;
         } else {
@@ -639,6 +682,7 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
             e = enqueue_copy(h, slot, io.layer);
             if (e == hipSuccess) e = hipStreamWaitEvent(st, h->ev_ready[slot], 0);
             h->stats.sync_loads++;
+            log_msg(h, MOE_LOG_INFO, "layer " + std::to_string(io.layer) + ": not prefetched, loaded before compute");
         }
         if (e != hipSuccess) return hip_fail(h, e, "pool acquire");
         blob = h->pool + (uint64_t)slot * h->slot_bytes;
@@ -771,12 +815,14 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
             h->prefetch_counter++;
             if (h->fail_at && h->prefetch_counter == h->fail_at) {
                 h->stats.prefetch_failed++;   // forced failure: this layer will load synchronously
+                log_msg(h, MOE_LOG_WARN, "prefetch of layer " + std::to_string(y) + " failed (test hook): it will load synchronously");
                 continue;
             }
             e = enqueue_copy(h, v, y);
             if (e != hipSuccess) {
                 (void)hipGetLastError();
                 h->stats.prefetch_failed++;
+                log_msg(h, MOE_LOG_WARN, "prefetch of layer " + std::to_string(y) + " failed: it will load synchronously");
                 continue;
             }
             h->from_prefetch[v] = 1;
@@ -949,6 +995,7 @@ int stream_pool_configure(moe_prefill_t* h, stream_pool_params_t* inout)
     h->res_live = s.residents;
     h->depth_live = s.depth;
     h->reserve_bytes = p.reserve_bytes > 0 ? p.reserve_bytes : 0;
+    h->poison = getenv("MOE_DEBUG_POISON") && atoi(getenv("MOE_DEBUG_POISON"));
     h->active = -1;
     h->prefetch_counter = 0;
     const char* fa = getenv("MOE_TEST_PREFETCH_FAIL");
@@ -989,6 +1036,10 @@ int stream_pool_configure(moe_prefill_t* h, stream_pool_params_t* inout)
     h->stats.eff_residents = s.residents;
     h->stats.warnings = warn;
     write_struct(inout, p);
+    log_warnings(h, warn, "pool");
+    log_msg(h, MOE_LOG_INFO, "pool: " + std::to_string(s.slots) + " slots of " + std::to_string(slot_bytes) +
+            " bytes, depth " + std::to_string(s.depth) + ", " + std::to_string(s.residents) + " residents" +
+            (h->vmm ? " (one physical allocation per slot)" : " (one allocation)"));
     h->err.clear();
     return MOE_OK;
 }
@@ -1009,6 +1060,9 @@ int stream_pool_set_budget(moe_prefill_t* h, stream_pool_budget_t* inout)
     int w = 0;
     const int rc = pool_trim(h, p.max_vram_bytes, &rel, &w);
     h->warnings |= w;
+    log_warnings(h, w, "pool budget");
+    if (rel) log_msg(h, MOE_LOG_INFO, "pool budget: released " + std::to_string(rel) + " bytes, " +
+                     std::to_string(h->res_live) + " residents left");
     p.eff_slots = h->res_live + count_slots(h, kSlotStreaming);
     p.eff_depth = h->depth_live;
     p.eff_residents = h->res_live;
@@ -1017,6 +1071,15 @@ int stream_pool_set_budget(moe_prefill_t* h, stream_pool_budget_t* inout)
     write_struct(inout, p);
     if (rc != MOE_OK) return rc;
     h->err.clear();
+    return MOE_OK;
+}
+
+int moe_prefill_set_log(moe_prefill_t* h, moe_log_fn fn, void* user, int32_t level)
+{
+    if (!h) return fail(nullptr, MOE_EINVAL, "null handle");
+    h->log_fn = fn;
+    h->log_user = user;
+    h->log_level = level;
     return MOE_OK;
 }
 

@@ -21,6 +21,7 @@ MiB = 1 << 20
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"^typedef[^;]*;", "", src, flags=re.M | re.S)     # function-pointer types declare nothing
     names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
     return sorted(set(n for n in names if n not in ("defined",)))
 
@@ -54,6 +55,19 @@ def test_create_without_gpu_fails_clearly():
         mp.moe_prefill_create(256, 512, 8, 2, 64)
     assert ei.value.code in (mp.MOE_EUNSUPPORTED, mp.MOE_EHIP)
     assert mp.moe_prefill_last_error()
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error path")
+def test_errors_reach_stderr_when_MOE_LOG_LEVEL_is_set(capfd, monkeypatch):
+    monkeypatch.setenv("MOE_LOG_LEVEL", "0")
+    with pytest.raises(mp.MoePrefillError):
+        mp.moe_prefill_create(256, 512, 8, 2, 64)
+    err = capfd.readouterr().err
+    assert "moe_prefill error:" in err and mp.moe_prefill_last_error() in err
+    monkeypatch.setenv("MOE_LOG_LEVEL", "-1")
+    with pytest.raises(mp.MoePrefillError):
+        mp.moe_prefill_create(256, 512, 8, 2, 64)
+    assert "moe_prefill" not in capfd.readouterr().err
 
 
 def test_dimension_checks():

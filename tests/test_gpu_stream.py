@@ -343,3 +343,100 @@ def test_reserve_shrinks_the_pool_when_a_pass_starts(tiny5):
     assert s["pressure_trims"] == 1, s
     assert (s["eff_residents"], s["evicted_residents"], s["released_bytes"]) == (1, 2, 2 * slot)
     h.close()
+
+
+# ------------------------------------------------------ logging and debug ---
+
+def test_log_sink_reports_degradations_and_pool_decisions(tiny5):
+    msgs = []
+    h = make_handle(tiny5.w)
+    mp.moe_prefill_set_log(h, lambda lv, m: msgs.append((lv, m)), mp.MOE_LOG_INFO)
+    slot = _slot_bytes(tiny5)
+    os.environ["MOE_TEST_PREFETCH_FAIL"] = "2"
+    try:
+        _configure(h, tiny5, prefetch_depth=4, resident_layers=0, max_vram_bytes=3 * slot)
+    finally:
+        del os.environ["MOE_TEST_PREFETCH_FAIL"]
+    tiny5.check(tiny5.run_passes(h, 1))
+    mp.stream_pool_set_budget(h, 2 * slot)
+    text = "\n".join(m for _, m in msgs)
+    assert any(lv == mp.MOE_LOG_WARN and "prefetch depth reduced" in m for lv, m in msgs), text
+    assert any(lv == mp.MOE_LOG_WARN and "failed (test hook)" in m for lv, m in msgs), text
+    assert any(lv == mp.MOE_LOG_INFO and m.startswith("pool: 3 slots") for lv, m in msgs), text
+    assert any(lv == mp.MOE_LOG_INFO and "released" in m for lv, m in msgs), text
+    # WARN level drops the INFO messages; errors always come through
+    msgs.clear()
+    mp.moe_prefill_set_log(h, lambda lv, m: msgs.append((lv, m)), mp.MOE_LOG_WARN)
+    tiny5.check(tiny5.run_passes(h, 1))
+    assert all(lv <= mp.MOE_LOG_WARN for lv, _ in msgs)
+    with pytest.raises(mp.MoePrefillError):
+        mp.stream_pool_set_budget(h, 0)
+    assert msgs and msgs[-1][0] == mp.MOE_LOG_ERROR
+    mp.moe_prefill_set_log(h, None)
+    h.close()
+
+
+def _poisoned(st, **kw):
+    os.environ["MOE_DEBUG_POISON"] = "1"
+    try:
+        h = make_handle(st.w)
+        _configure(h, st, **kw)
+    finally:
+        del os.environ["MOE_DEBUG_POISON"]
+    return h
+
+
+def test_poisoned_slots_change_nothing(tiny5):
+    """Debug mode: a slot is filled with NaN bytes right before every refill, so a
+    read between a slot's free fence and its refill would turn outputs into NaN."""
+    h = _poisoned(tiny5, prefetch_depth=2, resident_layers=0, requested_slots=3)
+    tiny5.check(tiny5.run_passes(h, 2, order=[0, 1, 2, 3, 4, 2, 0]))
+    h.close()
+
+
+def test_poisoned_active_only_slots_never_read_unrouted_experts(skew4):
+    """Active-expert loads into a NaN-filled slot: the experts a layer routes no
+    rows to keep NaN bytes and must never be read."""
+    assert sum(_active_experts(skew4, l) for l in range(4)) < 4 * skew4.w.E
+    h = _poisoned(skew4, prefetch_depth=1, resident_layers=0, requested_slots=2, active_only=True)
+    skew4.check(skew4.run_passes(h, 2))
+    h.close()
+
+
+def test_serialized_launches_give_the_same_outputs(tiny5, tmp_path):
+    """Race check: the streamed stack in a child process with every kernel and copy
+    serialised by the runtime (AMD_SERIALIZE_KERNEL=3, AMD_SERIALIZE_COPY=3) equals the
+    reference bit for bit, as the normal overlapped run does."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = tmp_path / "y.npy"
+    code = f"""
+import sys
+sys.path.insert(0, {root!r}); sys.path.insert(0, {os.path.join(root, "tests")!r})
+import numpy as np, torch
+import moe_prefill_ffn_amd as mp, workload as wl
+from gpu_helpers import ExpertCache, host_blob, make_handle
+w = wl.Workload("stack5_T64_d256_f512_E8_top2", 64, 256, 512, 8, 2, 5, 600)
+blobs = [host_blob(w, ExpertCache(w, l, keep=False), pinned=True) for l in range(5)]
+h = make_handle(w)
+mp.stream_pool_configure(h, blobs, prefetch_depth=2, resident_layers=0, requested_slots=3)
+ys = []
+for p in range(2):
+    for l in range(5):
+        y = torch.empty(w.T, w.d, device="cuda")
+        x = torch.from_numpy(wl.layer_activations(w, l)).cuda()
+        lg = torch.from_numpy(wl.layer_logits(w, l)).cuda()
+        mp.moe_prefill_run_layer(h, x, lg, y, layer=l)
+        ys.append(y)
+torch.cuda.synchronize()
+np.save({str(out)!r}, np.stack([y.cpu().numpy() for y in ys]))
+h.close()
+"""
+    env = dict(os.environ, AMD_SERIALIZE_KERNEL="3", AMD_SERIALIZE_COPY="3")
+    say("[case] serialized child process")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0, r.stderr[-2000:]
+    ys = np.load(out)
+    for i, y in enumerate(ys):
+        assert_equal(f"serialized layer {i % 5}", y, tiny5.ref[i % 5])
