@@ -292,8 +292,10 @@ def summarize_trace(trace_dir: str, passes: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed layers first: the MI355X needs ~40 ms of sustained work to reach "
+                         "its steady clocks (a cold layer takes ~290 us, a warm one ~195 us)")
     ap.add_argument("--stream-passes", type=int, default=3)
     ap.add_argument("--cpu-reps", type=int, default=15)
     ap.add_argument("--no-stream", action="store_true")
