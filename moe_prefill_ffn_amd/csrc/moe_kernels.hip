@@ -102,8 +102,8 @@ __device__ __forceinline__ uint32_t q8_block_of8(float4 v, float* scale)
 // +0) << 32 | (2^32 - 1 - e), the order (larger logit first, ties to the lower
 // expert index) is the unsigned order of the 64-bit keys, and all keys differ.
 // Slot j of a token is the expert whose key has rank j.  Up to 128 experts the
-// ranks are counted directly (every lane compares its keys with all E keys,
-// broadcast from LDS); above that, each lane keeps the keys of experts lane,
+// ranks are counted directly (a workgroup per token, every key compared with all
+// E keys broadcast from LDS); above that, each lane keeps the keys of experts lane,
 // lane + 64, ... in registers and slot j is the wave-wide maximum key after
 // slots 0 .. j-1 were taken out (k rounds of a lane-local maximum and a 6-step
 // butterfly): O(E k) instead of O(E^2) compares.  Both give the same slots.
@@ -145,28 +145,41 @@ __device__ __forceinline__ void route_weights(int t, int k, float* __restrict__ 
     if (lane < k) wts[(int64_t)t * k + lane] = z / sum;
 }
 
-// E <= kRankMaxE: ranks counted against all keys (keys: this wave's LDS area)
+// E <= kRankMaxE: one token per workgroup.  Thread (e = tid % 128, part = tid / 128)
+// counts the keys of part `part` of the experts (the first or second half of
+// 0 .. E-1) that beat key e; the two partial ranks add up in LDS.  Splitting the
+// E^2 compares over four waves per token keeps every SIMD busy with several
+// routing waves instead of one long serial one.
 __device__ __forceinline__ void route_token_rank(const float* __restrict__ logits, int t, int E,
                                                  int k, int32_t* __restrict__ eidx,
                                                  float* __restrict__ wts,
                                                  uint32_t* __restrict__ mask, int W,
-                                                 uint64_t* keys, float* zsel)
+                                                 uint64_t* keys, int* prank, float* zsel)
 {
-    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
     const float* lt = logits + (int64_t)t * E;
-    for (int e = lane; e < E; e += 64) keys[e] = route_key(lt[e], e);
-    __builtin_amdgcn_wave_barrier();
-    for (int e = lane; e < E; e += 64) {
+    if (tid < E) keys[tid] = route_key(lt[tid], tid);
+    __syncthreads();
+    const int e = tid & (kRankMaxE - 1), part = tid >> 7;   // part: uniform per wave
+    const int hE = (E + 1) >> 1;
+    const int c0 = part ? hE : 0, c1 = part ? E : hE;
+    int rank = 0;
+    if (e < E) {
         const uint64_t me = keys[e];
-        int rank = 0;
-        for (int c = 0; c < E; ++c) rank += keys[c] > me ? 1 : 0;
+        for (int c = c0; c < c1; ++c) rank += keys[c] > me ? 1 : 0;
+        if (part) prank[e] = rank;
+    }
+    __syncthreads();
+    if (!part && e < E) {
+        rank += prank[e];
         if (rank < k) {
             eidx[(int64_t)t * k + rank] = e;
             zsel[rank] = lt[e];
             atomicOr(&mask[(int64_t)e * W + (t >> 5)], 1u << (t & 31));
         }
     }
-    route_weights(t, k, wts, zsel);
+    __syncthreads();
+    if (tid < 64) route_weights(t, k, wts, zsel);
 }
 
 template <int NK>   // keys per lane: E <= 64 * NK
@@ -226,15 +239,19 @@ __global__ __launch_bounds__(256) void k_route_quant(const float* __restrict__ l
                                                      int64_t n_blocks, int nbk, int dx_stride,
                                                      int8_t* __restrict__ xq, float* __restrict__ dx)
 {
-    __shared__ uint64_t keys[4][kRankMaxE];
+    __shared__ uint64_t keys[kRankMaxE];
+    __shared__ int prank[kRankMaxE];
     __shared__ float zsel[4][64];
     if ((int)blockIdx.x < n_route) {
-        const int wave = threadIdx.x >> 6;
+        if (E <= kRankMaxE) {                             // one token per workgroup
+            const int t = blockIdx.x;
+            if (t < T) route_token_rank(logits, t, E, k, eidx, wts, mask, W, keys, prank, zsel[0]);
+            return;
+        }
+        const int wave = threadIdx.x >> 6;                // one token per wave
         const int t = blockIdx.x * 4 + wave;
         if (t >= T) return;
-        if (E <= kRankMaxE)
-            route_token_rank(logits, t, E, k, eidx, wts, mask, W, keys[wave], zsel[wave]);
-        else if (E <= 256)
+        if (E <= 256)
             route_token<4>(logits, t, E, k, eidx, wts, mask, W, zsel[wave]);
         else
             route_token<kRouteKeys>(logits, t, E, k, eidx, wts, mask, W, zsel[wave]);
@@ -843,7 +860,7 @@ static inline void mark(const LayerLaunch& L, int i, hipStream_t st)
 hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
 {
     const int64_t R = (int64_t)L.T * L.k;
-    const int n_route = (int)nblk(L.T, 4);
+    const int n_route = L.E <= kRankMaxE ? L.T : (int)nblk(L.T, 4);   // routing workgroups
     const int64_t xblocks = (int64_t)L.T * (L.d / 32);
     mark(L, kRouteQuant, st);
     hipLaunchKernelGGL(k_route_quant, dim3(n_route + nblk(xblocks * 8, 256)), dim3(256), 0, st,
