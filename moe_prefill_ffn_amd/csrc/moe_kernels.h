@@ -24,6 +24,8 @@ struct GemmArgs {
     int E;                    // experts in the blob (tile expert indices are clamped to it)
     int gu_f;                 // f of the interleaved gate/up matrix (gate/up launch only)
     int a_scale_stride;       // floats per A_scale row (a multiple of the 8-block scale group)
+    const uint32_t* fold_flag;  // nonzero: some A scale is outside the range the 16x codes allow
+    uint32_t* h_flag;         // gate/up launch: set when an H block scale is outside that range
 };
 
 struct LayerLaunch {

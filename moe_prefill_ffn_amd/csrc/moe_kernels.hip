@@ -213,12 +213,22 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
     route_weights(t, k, wts, zsel);
 }
 
+// True when a nonzero block scale d lies outside [2^-98, 2^107] (NaN included).
+// Inside that range every product d * w_scale with a nonzero fp16 weight scale
+// (|w_scale| in [2^-24, 65504]) stays a normal fp32 number after a division by 16,
+// which the grouped GEMM's 16x codes rely on.
+__device__ __forceinline__ bool scale_outside_fold_range(float d)
+{
+    const float a = fabsf(d);
+    return d != 0.0f && !(a >= 0x1p-98f && a <= 0x1p107f);
+}
+
 // x is a flat array of n_blocks 32-float blocks (a row-major [rows, K] matrix
 // with K % 32 == 0); 8 lanes per block, 4 values per lane.
 // block blk = row * nbk + b; its scale goes to scale[row * stride + b]
 __device__ __forceinline__ void quant_block8(const float* __restrict__ x, int64_t blk, int nbk,
                                              int stride, int8_t* __restrict__ q,
-                                             float* __restrict__ scale)
+                                             float* __restrict__ scale, uint32_t* __restrict__ flag)
 {
     const int sub = threadIdx.x & 7;
     const float4 v = *reinterpret_cast<const float4*>(x + blk * 32 + sub * 4);
@@ -228,6 +238,7 @@ __device__ __forceinline__ void quant_block8(const float* __restrict__ x, int64_
     if (sub == 0) {
         const int64_t row = blk / nbk;
         scale[row * stride + (blk - row * nbk)] = d;
+        if (scale_outside_fold_range(d)) atomicOr(flag, 1u);
     }
 }
 
@@ -237,7 +248,8 @@ __global__ __launch_bounds__(256) void k_route_quant(const float* __restrict__ l
                                                      uint32_t* __restrict__ mask, int W,
                                                      int n_route, const float* __restrict__ x,
                                                      int64_t n_blocks, int nbk, int dx_stride,
-                                                     int8_t* __restrict__ xq, float* __restrict__ dx)
+                                                     int8_t* __restrict__ xq, float* __restrict__ dx,
+                                                     uint32_t* __restrict__ x_flag)
 {
     __shared__ uint64_t keys[kRankMaxE];
     __shared__ int prank[kRankMaxE];
@@ -259,7 +271,7 @@ __global__ __launch_bounds__(256) void k_route_quant(const float* __restrict__ l
     }
     const int64_t g = (int64_t)(blockIdx.x - n_route) * 256 + threadIdx.x;
     const int64_t blk = g >> 3;
-    if (blk < n_blocks) quant_block8(x, blk, nbk, dx_stride, xq, dx);   // whole 8-lane groups together
+    if (blk < n_blocks) quant_block8(x, blk, nbk, dx_stride, xq, dx, x_flag);   // whole 8-lane groups together
 }
 
 // ---------------------------------------------------------------- group ---
@@ -460,7 +472,14 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
 // gives the scale products a_scale[row] * w_scale[col] of both row halves (one
 // rounding each, as a plain fp32 multiply), and per row half one
 // v_mfma_i32_32x32x32_i8 gives the exact int32 block sums.  The VALU is left
-// with unpacking the nibbles and the convert + fma per element.  Both row
+// with unpacking the nibbles and the convert + fma per element.  The unpack
+// places each 4-bit code in the high half of a byte (16x the weight), and the
+// fp16 weight scale is divided by 16 in fp32 to match: 16 isum * (a_scale *
+// w_scale / 16) is the same real product as isum * a_scale * w_scale, and with
+// every nonzero A scale in [2^-98, 2^107] the scale product stays a normal
+// number, so its rounding is that of the unscaled one.  The producers of the A
+// scales flag any scale outside that range; a launch that sees the flag takes
+// the plain unpack (kFold = false) and the exact unscaled arithmetic.  Both row
 // halves' integer MFMAs are issued before the first half's convert + fma, so the
 // second one runs under that VALU work; a wave stays at 122 VGPRs (four waves
 // per SIMD).  A partly filled half converts only the 8-row register groups that
@@ -483,6 +502,31 @@ typedef float v32f __attribute__((ext_vector_type(32)));
 __device__ __forceinline__ uint32_t nib_to_i8(uint32_t v)   // 4 offset-binary nibbles -> 4 int8
 {
     return (v + 0x78787878u) ^ 0x80808080u;
+}
+// 8 offset-binary nibbles (code = q + 8) -> two words of 4 int8 each holding 16 * q:
+// the code with its top bit flipped is q in 4-bit two's complement, and in the high
+// half of a byte it reads as 16 * q.  Three instructions per 8 codes instead of seven.
+__device__ __forceinline__ uint32_t nib_hi_i8x16(uint32_t w) { return (w & 0xF0F0F0F0u) ^ 0x80808080u; }
+__device__ __forceinline__ uint32_t nib_lo_i8x16(uint32_t w) { return ((w << 4) & 0xF0F0F0F0u) ^ 0x80808080u; }
+
+// B operand of one 32-block: codes of k 0-3 | 4-7 in w0 and 8-11 | 12-15 in w1
+// (low | high nibbles).  kFold: the 16x form.
+template <bool kFold>
+__device__ __forceinline__ v4i unpack_b(uint32_t w0, uint32_t w1)
+{
+    v4i b;
+    if (kFold) {
+        b.x = (int)nib_lo_i8x16(w0);
+        b.y = (int)nib_hi_i8x16(w0);
+        b.z = (int)nib_lo_i8x16(w1);
+        b.w = (int)nib_hi_i8x16(w1);
+    } else {
+        b.x = (int)nib_to_i8(w0 & 0x0F0F0F0Fu);
+        b.y = (int)nib_to_i8((w0 >> 4) & 0x0F0F0F0Fu);
+        b.z = (int)nib_to_i8(w1 & 0x0F0F0F0Fu);
+        b.w = (int)nib_to_i8((w1 >> 4) & 0x0F0F0F0Fu);
+    }
+    return b;
 }
 
 // Direct global->LDS loads: lane i's 16 bytes from g land at LDS wave_base + 16 i.
@@ -563,16 +607,26 @@ __device__ __forceinline__ void swiglu_q8_epilogue(const GemmArgs& g, uint8_t* l
         float d;
         const uint32_t packed = q8_block_of8(hv, &d);
         *reinterpret_cast<uint32_t*>(g.hq + r * f + fblk * 32 + sub * 4) = packed;
-        if (sub == 0) g.dh[r * g.dh_stride + fblk] = d;
+        if (sub == 0) {
+            g.dh[r * g.dh_stride + fblk] = d;
+            if (scale_outside_fold_range(d)) atomicOr(g.h_flag, 1u);
+        }
     }
 }
 
+// The work item of a workgroup: row tile (expert, first row, rows) and n-group.
+struct GemmItem {
+    int ng, e, r0, nrows;
+};
+
+// XCD x (dispatch is round-robin over the 8 XCDs) takes a contiguous range of row
+// tiles, all their n-groups (gate/up: the tiles of more than 32 rows first).
+// False: this workgroup has no item.  Runs before the kernel picks its arithmetic
+// path, so the tile-list reads stay scalar loads.
 template <bool kGateUp>
-__device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
+__device__ __forceinline__ bool gemm_item(const GemmArgs& g, GemmItem& it)
 {
     const int NG = ((g.N >> 5) + 3) >> 2;                 // n-groups of 4 n-tiles
-    // XCD x (dispatch is round-robin over the 8 XCDs) takes a contiguous range of
-    // row tiles, all their n-groups (gate/up: the tiles of more than 32 rows first)
     int tile, ng;
     {
         const int nt_all = *g.ntiles;
@@ -580,7 +634,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
         const int tq = nt_all >> 3, tr = nt_all & 7;
         const int ta = xcd * tq + (xcd < tr ? xcd : tr);
         const int tn = tq + (xcd < tr ? 1 : 0);
-        if (slot >= tn * NG) return;                      // uniform across the workgroup
+        if (slot >= tn * NG) return false;                // uniform across the workgroup
         if (kGateUp) {
             int heavy = 0;
             for (int t = ta; t < ta + tn; ++t) heavy += (g.tiles[3 * t + 2] - g.tiles[3 * t + 1]) > 32;
@@ -603,11 +657,18 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
             ng = slot - (slot / NG) * NG;
         }
     }
-
     const int te = g.tiles[3 * tile + 0];
-    const int e = te < 0 ? 0 : (te >= g.E ? g.E - 1 : te); // always valid; a no-op for a sound list
-    const int r0 = g.tiles[3 * tile + 1];
-    const int nrows = g.tiles[3 * tile + 2] - r0;          // 1 .. kBM
+    it.ng = ng;
+    it.e = te < 0 ? 0 : (te >= g.E ? g.E - 1 : te);      // always valid; a no-op for a sound list
+    it.r0 = g.tiles[3 * tile + 1];
+    it.nrows = g.tiles[3 * tile + 2] - it.r0;            // 1 .. kBM
+    return true;
+}
+
+template <bool kGateUp, bool kFold>
+__device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g, const GemmItem& it, uint8_t* lds)
+{
+    const int ng = it.ng, e = it.e, r0 = it.r0, nrows = it.nrows;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int K = g.K, N = g.N;
@@ -616,7 +677,6 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
     const bool wave_on = nt_real < (N >> 5);
     const int nt = wave_on ? nt_real : (N >> 5) - 1;      // idle waves load valid memory
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kRing * kStageBytes + 2 * kScaleBytes];
     uint8_t* const ring = lds;
     uint8_t* const sbuf = lds + kRing * kStageBytes;
 
@@ -717,18 +777,14 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
             // 0-31 carry block 0's scales, lanes 32-63 block 1's, rows 0-31 either way):
             // t[i] = block 0 products, t[16 + i] = block 1 products
             const uint16_t hb = *reinterpret_cast<const uint16_t*>(sc + ws_off + U * 4 + h * 2);
-            const float dw = (float)__builtin_bit_cast(_Float16, hb);
+            const float dw = (float)__builtin_bit_cast(_Float16, hb) * (kFold ? 0.0625f : 1.0f);
             const float dxv = *reinterpret_cast<const float*>(sc + xs_off1h + U * 8 + h * 4);
             const v32f t = __builtin_amdgcn_mfma_f32_32x32x1f32(dxv, dw, fzero, 0, 0, 0);
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const uint32_t w0 = q ? bq.z : bq.x;
                 const uint32_t w1 = q ? bq.w : bq.y;
-                v4i bop;
-                bop.x = (int)nib_to_i8(w0 & 0x0F0F0F0Fu);
-                bop.y = (int)nib_to_i8((w0 >> 4) & 0x0F0F0F0Fu);
-                bop.z = (int)nib_to_i8(w1 & 0x0F0F0F0Fu);
-                bop.w = (int)nib_to_i8((w1 >> 4) & 0x0F0F0F0Fu);
+                const v4i bop = unpack_b<kFold>(w0, w1);
                 const v4i a0 = *reinterpret_cast<const v4i*>(sb + kA_OFF + a_off0[q]);
                 const v16i is0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, bop, zero, 0, 0, 0);
                 fma_groups(std::integral_constant<int, 0>{}, acc0, is0, t, 16 * q, G);
@@ -742,13 +798,9 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
         for (int q = 0; q < 2; ++q) {
             const uint32_t w0 = q ? bq.z : bq.x;
             const uint32_t w1 = q ? bq.w : bq.y;
-            v4i bop;
-            bop.x = (int)nib_to_i8(w0 & 0x0F0F0F0Fu);
-            bop.y = (int)nib_to_i8((w0 >> 4) & 0x0F0F0F0Fu);
-            bop.z = (int)nib_to_i8(w1 & 0x0F0F0F0Fu);
-            bop.w = (int)nib_to_i8((w1 >> 4) & 0x0F0F0F0Fu);
+            const v4i bop = unpack_b<kFold>(w0, w1);
             const uint16_t hb = (uint16_t)(q ? (bs >> 16) : (bs & 0xffffu));
-            const float dw = (float)__builtin_bit_cast(_Float16, hb);
+            const float dw = (float)__builtin_bit_cast(_Float16, hb) * (kFold ? 0.0625f : 1.0f);
             // t[16*half + i] = a_scale(row of D element i in that half) * w_scale(col)
             const v32f t = __builtin_amdgcn_mfma_f32_32x32x1f32(q ? dx.y : dx.x, dw, fzero, 0, 0, 0);
             const v4i a0 = *reinterpret_cast<const v4i*>(sb + kA_OFF + a_off0[q]);
@@ -779,7 +831,12 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
             if (s0 + 3 < npairs) stage(two_c, full_c, std::integral_constant<int, 3>{}, s0 + 3, G);
         }
     };
-    if (nrows > 56)
+    if (!kFold) {                     // the rare exact path: two variants keep the code small
+        if (nrows > 32)
+            run(std::true_type{}, std::integral_constant<int, 4>{});
+        else
+            run(std::false_type{}, std::integral_constant<int, 0>{});
+    } else if (nrows > 56)
         run(std::true_type{}, std::integral_constant<int, 4>{});
     else if (nrows > 48)
         run(std::true_type{}, std::integral_constant<int, 3>{});
@@ -810,13 +867,36 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g)
 
 // gate/up projection: A rows gathered from Xq through the row table, output
 // columns in logical gate | up order.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_gate_up(GemmArgs g) { grouped_gemm_body<true>(g); }
+constexpr int kGemmLds = kRing * kStageBytes + 2 * kScaleBytes;   // 40 KiB: four workgroups per CU
+
+// The launch reads the scale flag once and runs one of the two instantiations; the
+// LDS is declared here, once, so both share it (a __shared__ array inside the
+// template would be allocated per instantiation).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_gate_up(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kGemmLds];
+    GemmItem it;
+    if (!gemm_item<true>(g, it)) return;
+    if (*g.fold_flag == 0)
+        grouped_gemm_body<true, true>(g, it, lds);
+    else
+        grouped_gemm_body<true, false>(g, it, lds);
+}
 // down projection: A = Hq in row-table order.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_down(GemmArgs g) { grouped_gemm_body<false>(g); }
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_down(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kGemmLds];
+    GemmItem it;
+    if (!gemm_item<false>(g, it)) return;
+    if (*g.fold_flag == 0)
+        grouped_gemm_body<false, true>(g, it, lds);
+    else
+        grouped_gemm_body<false, false>(g, it, lds);
+}
 
 // -------------------------------------------------------------- combine ---
 // y[t, :] = sum_j w[t, j] * dm[pos[t*k + j], :], j ascending, fma chain from 0.
-// Also clears the membership mask for the next layer (it is dead here).
+// Also clears the membership mask and the scale flags for the next layer (dead here).
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ dm,
                                                  const float* __restrict__ wts,
                                                  const int32_t* __restrict__ pos, int T, int k, int d,
@@ -865,7 +945,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     mark(L, kRouteQuant, st);
     hipLaunchKernelGGL(k_route_quant, dim3(n_route + nblk(xblocks * 8, 256)), dim3(256), 0, st,
                        L.logits, L.T, L.E, L.k, L.eidx, L.wts, L.mask, L.W, n_route, L.x, xblocks,
-                       L.d / 32, scale_stride(L.d), L.xq, L.dx);
+                       L.d / 32, scale_stride(L.d), L.xq, L.dx, L.mask + (int64_t)L.E * L.W);
     mark(L, kGroup, st);
     hipLaunchKernelGGL(k_group, dim3(L.E), dim3(kGroupThreads), 0, st, L.mask, L.W, L.wprefix,
                        L.counts);
@@ -899,6 +979,8 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     gu.K = L.d;
     gu.E = L.E;
     gu.gu_f = L.f;
+    gu.fold_flag = L.mask + (int64_t)L.E * L.W;           // X scales (set by k_route_quant)
+    gu.h_flag = L.mask + (int64_t)L.E * L.W + 1;           // H scales (set by this launch)
     mark(L, kGemmGateUp, st);
     const unsigned tiles8 = 8 * nblk(max_tiles_now, 8);   // every XCD's tile range, rounded up
     hipLaunchKernelGGL(k_gemm_gate_up, dim3(nblk(gu.N / 32, 4) * tiles8), dim3(256), 0, st, gu);
@@ -917,6 +999,8 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     dn.N = L.d;
     dn.K = L.f;
     dn.gu_f = 0;
+    dn.fold_flag = gu.h_flag;
+    dn.h_flag = nullptr;
     mark(L, kGemmDown, st);
     hipLaunchKernelGGL(k_gemm_down, dim3(nblk(dn.N / 32, 4) * tiles8), dim3(256), 0, st, dn);
     mark(L, kCombine, st);
@@ -926,7 +1010,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
 hipError_t launch_combine(const LayerLaunch& L, hipStream_t st)
 {
     const int64_t work = (int64_t)L.T * (L.d / 4);
-    const int64_t mw = (int64_t)L.E * L.W;
+    const int64_t mw = (int64_t)mask_words(L.E, L.W);    // the mask and the scale flags
     hipLaunchKernelGGL(k_combine, dim3(nblk(work > mw ? work : mw, 256)), dim3(256), 0, st, L.dm,
                        L.wts, L.pos, L.T, L.k, L.d, L.y, L.mask, mw);
     mark(L, kNumKernels, st);

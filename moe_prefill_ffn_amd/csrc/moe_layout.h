@@ -75,6 +75,12 @@ MOE_HD static inline int gu_logical_row(int nt, int j, int f)
 }
 
 // -------------------------------------------------------------- workspace ---
+// The membership mask [E][W] is followed by kScaleFlagWords words: flag 0 is set
+// when an X block scale, flag 1 when an H block scale, is zero-free and outside
+// [2^-98, 2^107] (see the grouped GEMM).  Both are cleared with the mask.
+constexpr int kScaleFlagWords = 2;
+MOE_HD static inline uint64_t mask_words(int E, int W) { return (uint64_t)E * W + kScaleFlagWords; }
+
 struct WsLayout {
     uint64_t eidx, wts, mask, wprefix, counts, bounds, tiles, ntiles, load_stats;
     uint64_t rows, pos, rtok, xq, dx, gu, hq, dh, dm;
@@ -93,7 +99,7 @@ static inline WsLayout ws_layout(int d, int f, int E, int k, int Tmax)
     auto take = [&](uint64_t bytes) { uint64_t at = o; o = align_up(o + bytes, 256); return at; };
     L.eidx = take(R * 4);
     L.wts = take(R * 4);
-    L.mask = take((uint64_t)E * L.W * 4);
+    L.mask = take(mask_words(E, L.W) * 4);
     L.wprefix = take((uint64_t)E * L.W * 4);
     L.counts = take((uint64_t)E * 4);
     L.bounds = take((uint64_t)(E + 1) * 4);

@@ -581,7 +581,7 @@ int moe_prefill_create(const moe_prefill_params_t* pin, moe_prefill_t** out)
         h->ws_owned = true;
     }
     e = hipStreamCreateWithFlags(&h->copy, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipMemset(h->ws + h->L.mask, 0, (size_t)h->E * h->L.W * 4);
+    if (e == hipSuccess) e = hipMemset(h->ws + h->L.mask, 0, (size_t)mask_words(h->E, h->L.W) * 4);
     if (e == hipSuccess) e = hipMemset(h->ws + h->L.load_stats, 0, 16);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
@@ -689,7 +689,7 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
     }
 
     if (h->mask_dirty) {   // a launch failed part-way: restore the grouping state first
-        e = launch_fill_u32(reinterpret_cast<uint32_t*>(h->ws + h->L.mask), (int64_t)h->E * h->L.W, 0u, st);
+        e = launch_fill_u32(reinterpret_cast<uint32_t*>(h->ws + h->L.mask), (int64_t)mask_words(h->E, h->L.W), 0u, st);
         if (e != hipSuccess) return hip_fail(h, e, "grouping state reset");
         h->mask_dirty = false;
     }

@@ -164,6 +164,41 @@ def test_tiny_and_huge_magnitudes():
     check_full_parity(w, g, ref)
 
 
+def test_out_of_range_block_scales_take_the_exact_gemm_path_layer_by_layer():
+    """The GEMMs' 16x weight codes are exact only while every nonzero A block scale
+    lies in [2^-98, 2^107]; the quantizers flag any other scale and the GEMM of that
+    layer takes the plain codes.  Layers with X scales, or only H scales, outside the
+    range alternate with ordinary ones on one handle: every layer bit-exact, so each
+    flag is raised when needed and cleared for the next layer."""
+    w = wl.small_workload(64, 128, 128, 8, 2, seed_base=11)
+    ex = ExpertCache(w, 0)
+    blob = host_blob(w, ex).cuda()
+    lg = wl.layer_logits(w, 0)
+    x0 = wl.layer_activations(w, 0)
+    x_tiny = x0 * np.float32(1e-30)
+    x_tiny[3] *= np.float32(1e-8)
+    cases = [("ordinary", x0, None), ("tiny H scales", x0 * np.float32(1e-20), "h_low"),
+             ("ordinary", x0, None), ("huge H scales", x0 * np.float32(1e17), "h_high"),
+             ("tiny X scales", x_tiny, "x_low"), ("ordinary", x0, None)]
+    h = make_handle(w)
+    for name, x, want in cases:
+        say(f"[case] {name}")
+        ref = oracle.layer(x, lg, w.k, ex, w.f)
+        dx, dh = np.abs(ref["dx"]), np.abs(ref["dh"])
+        lo, hi = np.float32(2.0 ** -98), np.float32(2.0 ** 107)
+        x_out = ((dx > 0) & ((dx < lo) | (dx > hi))).any()
+        h_low, h_high = ((dh > 0) & (dh < lo)).any(), (dh > hi).any()
+        # the case holds what its name says (checked on the oracle's scales)
+        assert x_out == (want == "x_low")
+        if want in ("h_low", "h_high"):
+            assert {"h_low": h_low, "h_high": h_high}[want] and not x_out
+        if want is None:
+            assert not (x_out or h_low or h_high)
+        g = run_layer_gpu(h, w, x, lg, blob)
+        check_full_parity(w, g, ref)
+    h.close()
+
+
 def test_fewer_tokens_than_max_and_repeat_runs_are_identical():
     w = wl.WORKLOADS["tiny"]
     x = wl.layer_activations(w, 0)
