@@ -349,22 +349,25 @@ __global__ __launch_bounds__(256) void k_expert_load(const uint8_t* __restrict__
 // of word t/32 before t routed to e) -- stable in p.  Every workgroup first
 // scans the E counts (E <= 1024: four per thread) into the group bounds in LDS;
 // workgroup 0 also writes the bounds and the GEMM row-tile list (expert, first
-// row, end row; kBM rows per tile; expert order) for the kernels that follow,
-// one tile per thread (its expert found by binary search over the experts'
-// first tiles: empty experts own no tiles).
+// row, end row; kBM rows per tile; expert order) for the kernels that follow, a
+// run of consecutive tiles per thread (the run's expert found by binary search
+// over the experts' first tiles: empty experts own no tiles), and the last
+// workgroup the order in which the gate/up launch takes the tiles.
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eidx, int64_t R, int k,
                                                  const uint32_t* __restrict__ mask,
                                                  const int32_t* __restrict__ wprefix,
                                                  const int32_t* __restrict__ counts, int E, int W,
                                                  int32_t* __restrict__ bounds,
                                                  int32_t* __restrict__ tiles,
+                                                 int32_t* __restrict__ gu_order,
                                                  int32_t* __restrict__ ntiles,
                                                  int32_t* __restrict__ rows, int32_t* __restrict__ pos,
                                                  int32_t* __restrict__ rtok)
 {
     __shared__ int s_bounds[kRouteMaxE];
     __shared__ int s_tfirst[kRouteMaxE + 1];              // first tile of each expert (writer)
-    __shared__ int s_wc[4], s_wt[4];
+    __shared__ int s_wc[4], s_wt[4], s_wh[4];
+    __shared__ int s_hstart[9];                           // heavy tiles before each XCD range
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool writer = blockIdx.x == 0;
     int c4[4], t4[4], sc = 0, st = 0;
@@ -417,22 +420,84 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
         *ntiles = all_t;
     }
     __syncthreads();
+    // tile tau belongs to the expert e with s_tfirst[e] <= tau < s_tfirst[e + 1]; each
+    // thread takes a run of consecutive tiles (a binary search for the run's first
+    // tile, then a walk).  Tiles of more than 32 rows are "heavy".
+    const int run = (all_t + 255) >> 8;
+    const int t0 = tid * run, t1 = t0 + run < all_t ? t0 + run : all_t;
+    int lo0 = 0;
+    if (t0 < t1) {
+        int hi = E - 1;
+        while (lo0 < hi) {
+            const int mid = (lo0 + hi + 1) >> 1;
+            if (s_tfirst[mid] <= t0)
+                lo0 = mid;
+            else
+                hi = mid - 1;
+        }
+    }
+    auto tile_rows = [&](int tau, int& lo, int& r0, int& r1) {
+        while (lo + 1 < E && s_tfirst[lo + 1] <= tau) ++lo;
+        r0 = s_bounds[lo] + (tau - s_tfirst[lo]) * kBM;
+        const int rend = lo + 1 < E ? s_bounds[lo + 1] : all_c;
+        r1 = r0 + kBM < rend ? r0 + kBM : rend;
+    };
     if (writer) {
-        // tile tau belongs to the expert e with s_tfirst[e] <= tau < s_tfirst[e + 1]
-        for (int tau = tid; tau < all_t; tau += 256) {
-            int lo = 0, hi = E - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (s_tfirst[mid] <= tau)
-                    lo = mid;
-                else
-                    hi = mid - 1;
-            }
-            const int r0 = s_bounds[lo] + (tau - s_tfirst[lo]) * kBM;
-            const int rend = lo + 1 < E ? s_bounds[lo + 1] : all_c;
+        int lo = lo0, r0, r1;
+        for (int tau = t0; tau < t1; ++tau) {
+            tile_rows(tau, lo, r0, r1);
             tiles[3 * tau + 0] = lo;
             tiles[3 * tau + 1] = r0;
-            tiles[3 * tau + 2] = r0 + kBM < rend ? r0 + kBM : rend;
+            tiles[3 * tau + 2] = r1;
+        }
+    }
+    if (blockIdx.x == gridDim.x - 1) {
+        // gate/up launch order (the last workgroup, beside the writer): the tiles are
+        // split over the 8 XCDs in contiguous ranges, as the GEMMs split them; inside
+        // each range the heavy tiles come first, both kinds in tile order.
+        int lo = lo0, r0, r1, nheavy = 0;
+        for (int tau = t0; tau < t1; ++tau) {
+            tile_rows(tau, lo, r0, r1);
+            nheavy += r1 - r0 > 32;
+        }
+        int hincl = nheavy;                               // heavy tiles up to this run's end
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(hincl, o);
+            if (lane >= o) hincl += y;
+        }
+        if (lane == 63) s_wh[wave] = hincl;
+        const int tq = all_t >> 3, tr = all_t & 7;
+        auto range_start = [&](int x) { return x * tq + (x < tr ? x : tr); };
+        __syncthreads();
+        int hb = hincl - nheavy, htot = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            hb += i < wave ? s_wh[i] : 0;
+            htot += s_wh[i];
+        }
+        if (tid <= 8) s_hstart[tid] = htot;               // ranges that start at all_t
+        __syncthreads();
+        lo = lo0;
+        int h = hb;
+        for (int tau = t0; tau < t1; ++tau) {             // heavy tiles before each range start
+            for (int x = 0; x < 8; ++x)
+                if (range_start(x) == tau) s_hstart[x] = h;
+            tile_rows(tau, lo, r0, r1);
+            h += r1 - r0 > 32;
+        }
+        __syncthreads();
+        lo = lo0;
+        h = hb;
+        for (int tau = t0; tau < t1; ++tau) {
+            int x = 7;
+            while (range_start(x) > tau) --x;              // the range holding tau
+            tile_rows(tau, lo, r0, r1);
+            const bool heavy = r1 - r0 > 32;
+            const int ta = range_start(x), hx = h - s_hstart[x];
+            const int nh = s_hstart[x + 1] - s_hstart[x];
+            gu_order[heavy ? ta + hx : ta + nh + (tau - ta - hx)] = tau;
+            h += heavy;
         }
     }
     const int64_t p = (int64_t)blockIdx.x * 256 + tid;
@@ -635,23 +700,11 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs& g, GemmItem& it)
         const int ta = xcd * tq + (xcd < tr ? xcd : tr);
         const int tn = tq + (xcd < tr ? 1 : 0);
         if (slot >= tn * NG) return false;                // uniform across the workgroup
-        if (kGateUp) {
-            int heavy = 0;
-            for (int t = ta; t < ta + tn; ++t) heavy += (g.tiles[3 * t + 2] - g.tiles[3 * t + 1]) > 32;
-            const bool want_heavy = slot < heavy * NG;
-            const int rel = want_heavy ? slot : slot - heavy * NG;
-            int k = rel / NG;
-            ng = rel - k * NG;
-            tile = ta;
-            for (int t = ta; t < ta + tn; ++t) {
-                if (((g.tiles[3 * t + 2] - g.tiles[3 * t + 1]) > 32) == want_heavy) {
-                    if (k == 0) {
-                        tile = t;
-                        break;
-                    }
-                    --k;
-                }
-            }
+        if (kGateUp) {                                    // heavy tiles first in each range
+            const int k = slot / NG;
+            ng = slot - k * NG;
+            const int o = g.order[ta + k];
+            tile = o < 0 ? 0 : (o >= nt_all ? nt_all - 1 : o);   // a no-op for a sound order
         } else {
             tile = ta + slot / NG;
             ng = slot - (slot / NG) * NG;
@@ -955,7 +1008,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
                            L.E, L.expert_stride, L.load_stats);
     mark(L, kScatter, st);
     hipLaunchKernelGGL(k_scatter, dim3(nblk(R, 256)), dim3(256), 0, st, L.eidx, R, L.k, L.mask,
-                       L.wprefix, L.counts, L.E, L.W, L.bounds, L.tiles, L.ntiles, L.rows, L.pos,
+                       L.wprefix, L.counts, L.E, L.W, L.bounds, L.tiles, L.gu_order, L.ntiles, L.rows, L.pos,
                        L.rtok);
     const int max_tiles_now = (int)((R + kBM - 1) / kBM) + (L.E < R ? L.E : (int)R);
 
@@ -969,6 +1022,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     gu.q_off = L.gu_q_off;
     gu.s_off = L.gu_s_off;
     gu.tiles = L.tiles;
+    gu.order = L.gu_order;
     gu.ntiles = L.ntiles;
     gu.out = L.keep_gu ? L.gu : nullptr;
     gu.hq = L.hq;
