@@ -38,6 +38,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -54,9 +55,14 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and blank space taken out, so that
+    an edit of the comments alone keeps the recorded counter runs valid."""
     h = hashlib.sha256()
     for f in ("moe_kernels.hip", "moe_kernels.h", "moe_layout.h"):
-        h.update(open(os.path.join(ROOT, "moe_prefill_ffn_amd", "csrc", f), "rb").read())
+        text = open(os.path.join(ROOT, "moe_prefill_ffn_amd", "csrc", f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

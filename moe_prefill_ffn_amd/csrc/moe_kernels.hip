@@ -95,8 +95,10 @@ __device__ __forceinline__ uint32_t q8_block_of8(float4 v, float* scale)
 }
 
 // ------------------------------------------------------- route + quantise ---
-// One launch, two kinds of workgroup.  Workgroups [0, n_route) route 4 tokens
-// each (one wave per token); the rest quantise X to Q8.
+// One launch, two kinds of workgroup.  Workgroups [0, n_route) route tokens (up
+// to 128 experts one token per workgroup, above that 4 per workgroup, one per
+// wave); the rest quantise X to Q8 and flag block scales outside the range the
+// GEMMs' 16x weight codes allow.
 //
 // Routing: with key(e) = (order-preserving bits of the logit, with -0 read as
 // +0) << 32 | (2^32 - 1 - e), the order (larger logit first, ties to the lower
@@ -546,7 +548,7 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
 // scales flag any scale outside that range; a launch that sees the flag takes
 // the plain unpack (kFold = false) and the exact unscaled arithmetic.  Both row
 // halves' integer MFMAs are issued before the first half's convert + fma, so the
-// second one runs under that VALU work; a wave stays at 122 VGPRs (four waves
+// second one runs under that VALU work; a wave stays at 123 VGPRs (four waves
 // per SIMD).  A partly filled half converts only the 8-row register groups that
 // hold rows of the tile.
 //
