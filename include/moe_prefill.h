@@ -354,7 +354,7 @@ enum {
     MOE_K_ROUTE_QUANT = 0,    /* top-k routing, router weights, membership mask; Xq = Q8(x) */
     MOE_K_GROUP = 1,          /* per-expert row counts and membership-word prefixes */
     MOE_K_EXPERT_LOAD = 2,    /* active-expert load of a streamed layer (active_only pools) */
-    MOE_K_SCATTER = 3,        /* group bounds, GEMM row tiles and gate/up tile order, row table */
+    MOE_K_SCATTER = 3,        /* group bounds, GEMM row tiles and their order, row table */
     MOE_K_GEMM_GATE_UP = 4,   /* GU grouped GEMM with the SwiGLU + Q8 epilogue: Hq, its scales */
     MOE_K_GEMM_DOWN = 5,      /* Dm grouped GEMM */
     MOE_K_COMBINE = 6         /* y = weighted combine */

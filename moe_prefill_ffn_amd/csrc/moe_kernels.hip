@@ -354,14 +354,14 @@ __global__ __launch_bounds__(256) void k_expert_load(const uint8_t* __restrict__
 // row, end row; kBM rows per tile; expert order) for the kernels that follow, a
 // run of consecutive tiles per thread (the run's expert found by binary search
 // over the experts' first tiles: empty experts own no tiles), and the last
-// workgroup the order in which the gate/up launch takes the tiles.
+// workgroup the order in which the GEMM launches take the tiles.
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eidx, int64_t R, int k,
                                                  const uint32_t* __restrict__ mask,
                                                  const int32_t* __restrict__ wprefix,
                                                  const int32_t* __restrict__ counts, int E, int W,
                                                  int32_t* __restrict__ bounds,
                                                  int32_t* __restrict__ tiles,
-                                                 int32_t* __restrict__ gu_order,
+                                                 int32_t* __restrict__ tile_order,
                                                  int32_t* __restrict__ ntiles,
                                                  int32_t* __restrict__ rows, int32_t* __restrict__ pos,
                                                  int32_t* __restrict__ rtok)
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
         }
     }
     if (blockIdx.x == gridDim.x - 1) {
-        // gate/up launch order (the last workgroup, beside the writer): the tiles are
+        // GEMM tile order (the last workgroup, beside the writer): the tiles are
         // split over the 8 XCDs in contiguous ranges, as the GEMMs split them; inside
         // each range the heavy tiles come first, both kinds in tile order.
         int lo = lo0, r0, r1, nheavy = 0;
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
             const bool heavy = r1 - r0 > 32;
             const int ta = range_start(x), hx = h - s_hstart[x];
             const int nh = s_hstart[x + 1] - s_hstart[x];
-            gu_order[heavy ? ta + hx : ta + nh + (tau - ta - hx)] = tau;
+            tile_order[heavy ? ta + hx : ta + nh + (tau - ta - hx)] = tau;
             h += heavy;
         }
     }
@@ -555,8 +555,8 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
 // Workgroups are numbered so that each XCD (dispatch is round-robin over the
 // 8 XCDs) receives a contiguous run of row tiles with all their n-groups: the
 // n-groups of a row tile and the row tiles of an expert share that XCD's L2.
-// Inside an XCD's run the gate/up launch takes the tiles of more than 32 rows
-// first, so its workgroups that start last are the cheaper half-height ones.
+// Inside an XCD's run both launches take the tiles of more than 32 rows first,
+// so the workgroups that start last are the cheaper half-height ones.
 constexpr int kRing = 4;                  // LDS stages = stages per scale group
 constexpr int kA_OFF = 0;                 // [64 rows][4 chunks of 16 B], chunks swizzled per row
 constexpr int kB_OFF = 4096;              // [4 waves][64 lanes][16 B]
@@ -687,10 +687,9 @@ struct GemmItem {
 };
 
 // XCD x (dispatch is round-robin over the 8 XCDs) takes a contiguous range of row
-// tiles, all their n-groups (gate/up: the tiles of more than 32 rows first).
+// tiles, all their n-groups, the tiles of more than 32 rows first.
 // False: this workgroup has no item.  Runs before the kernel picks its arithmetic
 // path, so the tile-list reads stay scalar loads.
-template <bool kGateUp>
 __device__ __forceinline__ bool gemm_item(const GemmArgs& g, GemmItem& it)
 {
     const int NG = ((g.N >> 5) + 3) >> 2;                 // n-groups of 4 n-tiles
@@ -702,15 +701,10 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs& g, GemmItem& it)
         const int ta = xcd * tq + (xcd < tr ? xcd : tr);
         const int tn = tq + (xcd < tr ? 1 : 0);
         if (slot >= tn * NG) return false;                // uniform across the workgroup
-        if (kGateUp) {                                    // heavy tiles first in each range
-            const int k = slot / NG;
-            ng = slot - k * NG;
-            const int o = g.order[ta + k];
-            tile = o < 0 ? 0 : (o >= nt_all ? nt_all - 1 : o);   // a no-op for a sound order
-        } else {
-            tile = ta + slot / NG;
-            ng = slot - (slot / NG) * NG;
-        }
+        const int k = slot / NG;                          // heavy tiles first in each range
+        ng = slot - k * NG;
+        const int o = g.order[ta + k];
+        tile = o < 0 ? 0 : (o >= nt_all ? nt_all - 1 : o);   // a no-op for a sound order
     }
     const int te = g.tiles[3 * tile + 0];
     it.ng = ng;
@@ -931,7 +925,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kGemmLds];
     GemmItem it;
-    if (!gemm_item<true>(g, it)) return;
+    if (!gemm_item(g, it)) return;
     if (*g.fold_flag == 0)
         grouped_gemm_body<true, true>(g, it, lds);
     else
@@ -942,7 +936,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kGemmLds];
     GemmItem it;
-    if (!gemm_item<false>(g, it)) return;
+    if (!gemm_item(g, it)) return;
     if (*g.fold_flag == 0)
         grouped_gemm_body<false, true>(g, it, lds);
     else
@@ -1010,7 +1004,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
                            L.E, L.expert_stride, L.load_stats);
     mark(L, kScatter, st);
     hipLaunchKernelGGL(k_scatter, dim3(nblk(R, 256)), dim3(256), 0, st, L.eidx, R, L.k, L.mask,
-                       L.wprefix, L.counts, L.E, L.W, L.bounds, L.tiles, L.gu_order, L.ntiles, L.rows, L.pos,
+                       L.wprefix, L.counts, L.E, L.W, L.bounds, L.tiles, L.tile_order, L.ntiles, L.rows, L.pos,
                        L.rtok);
     const int max_tiles_now = (int)((R + kBM - 1) / kBM) + (L.E < R ? L.E : (int)R);
 
@@ -1024,7 +1018,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     gu.q_off = L.gu_q_off;
     gu.s_off = L.gu_s_off;
     gu.tiles = L.tiles;
-    gu.order = L.gu_order;
+    gu.order = L.tile_order;                              // the down launch keeps it
     gu.ntiles = L.ntiles;
     gu.out = L.keep_gu ? L.gu : nullptr;
     gu.hq = L.hq;

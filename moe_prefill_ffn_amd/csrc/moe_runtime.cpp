@@ -721,7 +721,7 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
     LL.counts = reinterpret_cast<int32_t*>(w + h->L.counts);
     LL.bounds = reinterpret_cast<int32_t*>(w + h->L.bounds);
     LL.tiles = reinterpret_cast<int32_t*>(w + h->L.tiles);
-    LL.gu_order = reinterpret_cast<int32_t*>(w + h->L.gu_order);
+    LL.tile_order = reinterpret_cast<int32_t*>(w + h->L.tile_order);
     LL.ntiles = reinterpret_cast<int32_t*>(w + h->L.ntiles);
     LL.rows = reinterpret_cast<int32_t*>(w + h->L.rows);
     LL.pos = reinterpret_cast<int32_t*>(w + h->L.pos);
