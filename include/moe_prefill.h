@@ -216,7 +216,7 @@ typedef struct stream_pool_params {
  *    slots of the same size are tried (residents first, then depth) down to
  *    one; if one slot fails: MOE_ENOMEM;
  *  - resident layers are uploaded before returning;
- *  - active_only (the survey's "active-expert-only streaming"): the layer's
+ *  - active_only (copy only the experts that receive rows): the layer's
  *    routing decides its copy.  After the grouping step of moe_prefill_run_layer
  *    a kernel reads the experts with rows > 0 straight from the pinned host blob
  *    (PCIe reads by the GPU, no host round trip) into the slot; experts without
