@@ -54,6 +54,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# how the streamed legs' overlap figures relate (hidden = copy + compute - wall time)
+OVERLAP_NOTE = ("copy_hidden_frac = hidden / copy can be at most compute / copy "
+                "(copy_hidden_frac_max) when the copies take longer than the compute; "
+                "overlap_efficiency = hidden / min(copy, compute) is the share of the "
+                "possible overlap achieved")
+
+
 def kernel_source_hash() -> str:
     """Hash of the kernel sources with comments and blank space taken out, so that
     an edit of the comments alone keeps the recorded counter runs valid."""
@@ -173,7 +180,9 @@ def stack_leg(mp, wl, torch, dev, key: str, passes: int) -> dict:
         "pcie_roofline_frac": round((moved / pcie) / t_wall, 4) if pcie > 0 else None,
         "copy_ms_per_pass": round(t_copy * 1e3, 3), "compute_ms_per_pass": round(t_comp_all * 1e3, 3),
         "copy_hidden_frac": round(hidden / t_copy, 4) if t_copy > 0 else None,
+        "copy_hidden_frac_max": round(min(1.0, t_comp_all / t_copy), 4) if t_copy > 0 else None,
         "overlap_efficiency": round(hidden / min(t_copy, t_comp_all), 4) if t_copy > 0 else None,
+        "overlap_note": OVERLAP_NOTE,
         "prefetch_activated": (s1["prefetch_activated"] - s0["prefetch_activated"]) / passes,
         "sync_loads": (s1["sync_loads"] - s0["sync_loads"]) / passes,
         "resident_layer": {
@@ -515,7 +524,9 @@ def main() -> int:
             "pcie_h2d_GBs_measured": round(ws.n_layers * lb / t_copy / 1e9, 2),
             "copy_ms_per_pass": round(t_copy * 1e3, 3), "compute_ms_per_pass": round(t_comp * 1e3, 3),
             "copy_hidden_frac": round(hidden / t_copy, 4),
+            "copy_hidden_frac_max": round(min(1.0, t_comp / t_copy), 4),
             "overlap_efficiency": round(hidden / min(t_copy, t_comp), 4),
+            "overlap_note": OVERLAP_NOTE,
             "prefetch_activated": s1["prefetch_activated"] - s0["prefetch_activated"],
             "sync_loads": s1["sync_loads"] - s0["sync_loads"],
         }
