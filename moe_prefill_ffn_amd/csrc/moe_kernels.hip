@@ -347,6 +347,7 @@ __global__ __launch_bounds__(256) void k_expert_load(const uint8_t* __restrict__
     }
 }
 
+// ------------------------------------------------------------ row table ---
 // Row table: pair p = t*k + j goes to row bounds[e] + prefix[e][t/32] + (tokens
 // of word t/32 before t routed to e) -- stable in p.  Every workgroup first
 // scans the E counts (E <= 1024: four per thread) into the group bounds in LDS;
