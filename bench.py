@@ -2,24 +2,30 @@
 """Benchmark of the MoE prompt (prefill) FFN layer on one MI355X.
 
 One step = one whole layer through the C ABI (route + Xq, group, row table,
-GU grouped GEMM with SwiGLU+requant, down grouped GEMM, combine) on the resident real-shape
-layer: T=1024 tokens, d_model=2048, d_ff=768, E=128 experts, top-8, Q4
-weights resident in HBM, synthetic seeded inputs.  The headline value is
-tokens/s per layer.
+GU grouped GEMM with SwiGLU+requant, down grouped GEMM, combine).  The headline
+is the largest configuration that fits one GPU: one resident layer of the
+skewed stack's shape, T=8192 tokens, d_model=4096, d_ff=1536, E=256 experts,
+top-8, Zipf(1.1) expert skew, Q4 weights resident in HBM, synthetic seeded
+inputs.  value = tokens/s per layer.
 
 Also reported on the same line:
-  roofline      the gate/up grouped GEMM (the dominant kernel): algorithmic
-                int8 ops per launch / its mean device time, measured with HIP
-                events on the launch stream over a timed region of K steps,
-                against the int8 MFMA dense peak (5.0 POPS)
-  kernels       mean device time of every kernel of the layer (same region)
-  graph_replay  the same layer captured once in a HIP graph and replayed K times
-  streamed      the 4-layer streamed stack (same shape, 2-slot pool, depth-1
+  roofline      the gate/up grouped GEMM (the dominant kernel) of the headline
+                layer: algorithmic int8 ops per launch / its mean device time,
+                from HIP events on the launch stream over exactly the K timed
+                layers, against the int8 MFMA dense peak (5.0 POPS), and against
+                the measured MFMA-only peak and per-32-block epilogue ceiling
+  denominators  microbenchmarks (libmoe_micro.so): int8 MFMA peak, the block
+                epilogue ceiling in each arithmetic form, VALU instruction
+                costs, a device copy, fp32 atomic adds
+  resident_c1   the real-shape resident layer (T=1024, d_model=2048, d_ff=768,
+                E=128, top-8), whose GEMMs are HBM-bound: its roofline against
+                8 TB/s with the MFMA fraction beside it, per-kernel times, and
+                the same layer captured in a HIP graph and replayed
+  streamed      the 4-layer streamed stack (T=1024 shape, 2-slot pool, depth-1
                 prefetch): tokens/s per pass, achieved H2D GB/s, measured PCIe
                 GB/s, fraction of copy time hidden and overlap efficiency
   streamed_active_experts
-                the first three layers of the skewed stack (T=8192, d_model=4096,
-                d_ff=1536, E=256, Zipf routing) through a 2-slot pool:
+                the first three layers of the skewed stack through a 2-slot pool:
                 whole-layer streaming with depth-1 prefetch against active_only
                 loads (only the routed experts, copied by a kernel after the
                 routing): ms and GB per pass
@@ -28,7 +34,8 @@ Also reported on the same line:
                 stack (3 slots, depth 2): tokens/s per pass, H2D GB/s achieved against
                 the measured PCIe rate, copy-hidden fraction, overlap efficiency, and
                 the resident per-layer kernel times and GEMM rates at those shapes
-  cpu_baseline  the CPU oracle timed on this host's cores on the same layer
+  cpu_baseline  the CPU oracle timed on this host's cores on a bounded token
+                sample of the headline layer
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -304,6 +311,232 @@ def summarize_trace(trace_dir: str, passes: int) -> dict:
     return res
 
 
+def gate_up_bytes(w, active: int) -> int:
+    """Algorithmic HBM bytes of one gate/up launch: the active experts' Q4 gate/up weights
+    (codes + fp16 scales), Xq + its scales read, Hq + its scales and the row table written."""
+    R = w.T * w.k
+    wgu = active * (2 * w.f * w.d // 2 + 2 * w.f * (w.d // 32) * 2)
+    return wgu + w.T * w.d + w.T * (w.d // 32) * 4 + R * w.f + R * (w.f // 32) * 4 + R * 4
+
+
+def down_bytes(w, active: int) -> int:
+    """Algorithmic HBM bytes of one down launch: the active experts' Q4 down weights, Hq and
+    its scales read, Dm written."""
+    R = w.T * w.k
+    wd = active * (w.d * w.f // 2 + w.d * (w.f // 32) * 2)
+    return wd + R * w.f + R * (w.f // 32) * 4 + R * w.d * 4
+
+
+def resident_leg(mp, wl, torch, dev, key: str, steps: int, warmup: int, micro, graph: bool = False) -> dict:
+    """One resident layer of workload `key`, layer 0: W untimed layers, then K timed layers
+    with HIP events between the kernels on the launch stream (the per-kernel device times of
+    exactly the timed region), the gate/up GEMM's roofline and the memory-bound kernels' GB/s."""
+    w = wl.WORKLOADS[key]
+    T, d, f, E, k = w.T, w.d, w.f, w.E, w.k
+    R = T * k
+    log(f"[bench] {w.name}: generating inputs")
+    x = torch.from_numpy(wl.layer_activations(w, 0)).to(dev)
+    lg = torch.from_numpy(wl.layer_logits(w, 0)).to(dev)
+    blob_h = torch.empty(mp.moe_prefill_layer_bytes(d, f, E), dtype=torch.uint8)
+    mp.pack_layer(d, f, E, lambda e: wl.expert_weights(w, 0, e), blob_h, threads=max(1, min(16, os.cpu_count() or 1)))
+    blob = blob_h.to(dev)
+    del blob_h
+    y = torch.empty(T, d, device=dev)
+    h = mp.moe_prefill_create(d, f, E, k, T, device=0)
+    stream = torch.cuda.current_stream(dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    mp.moe_prefill_run_layer(h, x, lg, y, layer=-1, weights=blob, stream=stream, exports={"counts": counts})
+    active = int((counts.cpu() > 0).sum())
+
+    def step():
+        mp.moe_prefill_run_layer(h, x, lg, y, layer=-1, weights=blob, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    mp.moe_prefill_set_timing(h, True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kt = mp.moe_prefill_kernel_times(h, reset=True)
+    mp.moe_prefill_set_timing(h, False)
+    us = (t1 - t0) * 1e6 / steps
+    kern_us = {n: (ms / c * 1e3 if c else None) for n, (c, ms) in kt.items()}
+    gu_us, dn_us = kern_us["gemm_gate_up"], kern_us["gemm_down"]
+    ops_gu = 2.0 * R * (2 * f) * d           # int8 multiply-adds x 2, routed rows only
+    ops_dn = 2.0 * R * d * f
+    gu_tops = ops_gu / (gu_us * 1e-6) / 1e12
+    dn_tops = ops_dn / (dn_us * 1e-6) / 1e12
+    b_gu, b_dn = gate_up_bytes(w, active), down_bytes(w, active)
+    gu_gbs = b_gu / (gu_us * 1e-6) / 1e9
+    dn_gbs = b_dn / (dn_us * 1e-6) / 1e9
+    ridge = INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    mfma = {"achieved": round(gu_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+            "frac": round(gu_tops / INT8_PEAK_TOPS, 4)}
+    hbm_roof = {"achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gu_gbs / HBM_PEAK_GBS, 4)}
+    if micro:
+        mfma["frac_of_measured_mfma_peak"] = round(gu_tops / micro["int8_mfma_peak_TOPS_measured"], 4)
+        mfma["frac_of_epilogue_ceiling"] = round(gu_tops / micro["epilogue_ceiling_TOPS"], 4)
+        hbm_roof["frac_of_measured_copy"] = round(gu_gbs / micro["copy_GBs"], 4)
+    bound = "mfma" if ops_gu / b_gu > ridge else "hbm"
+    roofline = dict(mfma if bound == "mfma" else hbm_roof)
+    roofline.update({
+        "bound": bound, "traffic": load_traffic("gemm_gate_up", key), "kernel": "gemm_gate_up",
+        "workload": w.name, "ops_per_launch": ops_gu, "algorithmic_bytes_per_launch": b_gu,
+        "arithmetic_intensity_ops_per_byte": round(ops_gu / b_gu, 1), "ridge_ops_per_byte": round(ridge, 1),
+        "active_experts": active, "mean_us": round(gu_us, 2),
+        "dtype": "int8 x int4 -> int32 blocks, fp32 epilogue",
+        "note": "gate/up GEMM with the fused SwiGLU + Q8 epilogue (writes Hq, not GU); mean device time "
+                "from HIP events on the launch stream over the timed layers",
+    })
+    roofline["mfma" if bound == "hbm" else "hbm"] = hbm_roof if bound == "mfma" else mfma
+    q_bytes = T * E * 4 + R * 8 + T * d * 4 + T * d + T * (d // 32) * 4   # logits, eidx+w, X, Xq, dx
+    c_bytes = R * d * 4 + R * 8 + T * d * 4
+    out = {
+        "workload": w.name, "us_per_layer": round(us, 2), "tokens_per_s_per_layer": round(T / (us * 1e-6), 1),
+        "steps": steps, "warmup": warmup, "active_experts": active,
+        "kernels_us": {n: (round(v, 2) if v is not None else None) for n, v in kern_us.items()},
+        "roofline": roofline,
+        "gemm_down": {"TOPS": round(dn_tops, 2), "frac_of_int8_peak": round(dn_tops / INT8_PEAK_TOPS, 4),
+                      "GBs": round(dn_gbs, 1), "frac_of_hbm": round(dn_gbs / HBM_PEAK_GBS, 4),
+                      "algorithmic_bytes_per_launch": b_dn, "mean_us": round(dn_us, 2)},
+        "hbm": {"route_quant_GBs": round(q_bytes / (kern_us["route_quant"] * 1e-6) / 1e9, 1),
+                "combine_GBs": round(c_bytes / (kern_us["combine"] * 1e-6) / 1e9, 1),
+                "route_quant_bytes": q_bytes, "combine_bytes": c_bytes, "peak_GBs": HBM_PEAK_GBS},
+    }
+    if graph:
+        out["graph_replay"] = graph_leg(mp, torch, h, x, lg, y, blob, stream, steps, warmup, T)
+    h.close()
+    del blob, x, lg, y
+    torch.cuda.empty_cache()
+    return out
+
+
+def graph_leg(mp, torch, h, x, lg, y, blob, stream, steps, warmup, T) -> dict:
+    """The same resident layer captured once in a HIP graph and replayed (inputs in place)."""
+    try:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            mp.moe_prefill_run_layer(h, x, lg, y, layer=-1, weights=blob, stream=side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, capture_error_mode="thread_local"):
+            mp.moe_prefill_run_layer(h, x, lg, y, layer=-1, weights=blob)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        us_graph = (time.perf_counter() - t0) * 1e6 / steps
+        del g
+        return {"us_per_layer": round(us_graph, 2), "tokens_per_s_per_layer": round(T / (us_graph * 1e-6), 1)}
+    except Exception as ex:          # reported, never fatal: the direct path is the measurement
+        log(f"[bench] graph capture failed: {ex}")
+        return {"error": str(ex)[:200]}
+
+
+def cpu_leg(wl, w, seconds: float) -> dict:
+    """The CPU oracle as it stands, on the host's cores, on a bounded sample of the layer:
+    routing, grouping and Q8 of all T tokens plus every stage of the sampled tokens' rows.
+    A 64-token probe sizes the sample to about `seconds` of oracle time."""
+    import numpy as np
+
+    import oracle
+
+    x = wl.layer_activations(w, 0)
+    lg = wl.layer_logits(w, 0)
+    perm = np.random.default_rng(1234).permutation(w.T)
+    eidx, _ = oracle.route(lg, w.k)
+    cache = {}
+
+    def pregen(toks):               # inputs of the timed call, generated before it
+        for e in np.unique(eidx[toks]):
+            if int(e) not in cache:
+                cache[int(e)] = wl.expert_weights(w, 0, int(e))
+
+    def timed(toks):
+        pregen(toks)
+        t0 = time.perf_counter()
+        oracle.layer(x, lg, w.k, cache.__getitem__, w.f, tokens=toks)
+        return time.perf_counter() - t0
+
+    probe = perm[:64]
+    tp = timed(probe)
+    n = int(min(w.T, max(64, round(64 * seconds / max(tp, 1e-3)))))
+    toks = perm[:n]
+    t = timed(toks)
+    return {"value": round(n / t, 1), "unit": "tokens/s per layer", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} of the {w.T} tokens of {w.name} layer 0 (seeded random sample): routing, "
+                      f"grouping and Q8 of all tokens plus every stage of the sampled tokens' {n * w.k} rows, "
+                      f"{t:.1f} s (expert weights generated before the timed call)"}
+
+
+def micro_leg(torch, dev) -> dict:
+    """Measured denominators (libmoe_micro.so): the int8 MFMA peak, the per-32-block
+    epilogue ceiling of the grouped GEMMs in each arithmetic form (register-only loops:
+    MFMAs + the block epilogue, no memory), single-instruction VALU rates, a device copy
+    and fp32 atomic adds into scattered rows."""
+    from moe_prefill_ffn_amd import micro
+
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    spec_mac_clk = INT8_PEAK_TOPS * 1e12 / 2 / (n_cu * 4 * 2.4e9)   # MACs per clock per SIMD at the spec
+    out = {"n_cu": n_cu, "spec_int8_mac_per_clk_per_simd": round(spec_mac_clk, 1)}
+    micro.block("mfma_i8", 2000, n_cu)                                # warm the clocks
+    forms = {}
+    for name, iters in (("mfma_i8", 40000), ("cvt_fma_mscale", 20000), ("cvt_fma_vscale", 20000),
+                        ("sub_fma_vscale", 20000), ("sub_fma_mscale", 20000), ("pipe_cvt_fma", 20000),
+                        ("overlap_indep", 20000)):
+        for wps in (4, 2):
+            r = micro.block(name, iters, n_cu, wps)
+            macs_iter = (4 if name == "mfma_i8" else 2) * 32768
+            mac_clk = wps * macs_iter * iters / r["cycles_per_wave"]
+            forms[f"{name}@{wps}w"] = {
+                "TOPS": round(r["work"] / (r["ms"] * 1e-3) / 1e12, 1),
+                "frac_of_spec_peak": round(r["work"] / (r["ms"] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                "mac_per_clk_per_simd": round(mac_clk, 1),
+                "frac_of_spec_per_clock": round(mac_clk / spec_mac_clk, 4),
+                "clock_ghz": round(r["clock_ghz"], 3),
+            }
+    out["block_forms"] = forms
+    out["int8_mfma_peak_TOPS_measured"] = forms["mfma_i8@4w"]["TOPS"]
+    best = max((v["TOPS"], k) for k, v in forms.items()
+               if not k.startswith("mfma_i8") and not k.startswith("overlap_indep"))
+    out["epilogue_ceiling_TOPS"] = best[0]
+    out["epilogue_ceiling_form"] = best[1]
+    valu = {}
+    for name in ("valu_fma", "valu_cvt", "valu_sub"):
+        iters = 20000
+        r = micro.block(name, iters, n_cu, 4)
+        valu[name] = round(r["cycles_per_wave"] / (4 * 64 * iters), 3)   # SIMD cycles per wave64 instruction
+    out["valu_cycles_per_wave_instr"] = valu
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    r = micro.copy(dst, src, n_cu * 16, 10)
+    out["copy_GBs"] = round(r["work"] / (r["ms"] * 1e-3) / 1e9, 1)
+    del src, dst
+    rows, d, k = 8192, 2048, 8
+    g = torch.Generator().manual_seed(5)
+    perm = torch.randperm(rows, generator=g).to(torch.int32)
+    dst_row = (perm // k).to(dev)
+    srcm = torch.ones(rows, d, dtype=torch.float32, device=dev)
+    y = torch.zeros(rows // k, d, dtype=torch.float32, device=dev)
+    r = micro.atomic(srcm, dst_row, y, 10)
+    out["atomic_add_f32"] = {"rows": rows, "d": d, "dest_rows": rows // k, "ms": round(r["ms"], 4),
+                             "G_atomics_per_s": round(rows * d / (r["ms"] * 1e-3) / 1e9, 1),
+                             "GBs": round(r["work"] / (r["ms"] * 1e-3) / 1e9, 1)}
+    torch.cuda.synchronize()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,7 +545,9 @@ def main() -> int:
                     help="untimed layers first: the MI355X needs ~40 ms of sustained work to reach "
                          "its steady clocks (a cold layer takes ~290 us, a warm one ~195 us)")
     ap.add_argument("--stream-passes", type=int, default=3)
-    ap.add_argument("--cpu-reps", type=int, default=15)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline's token sample")
+    ap.add_argument("--no-micro", action="store_true", help="skip the microbenchmark denominators")
     ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--no-active", action="store_true", help="skip the active-expert streaming comparison")
     ap.add_argument("--no-cpu", action="store_true")
@@ -322,6 +557,8 @@ def main() -> int:
                     help="summarise rocprofv3 kernel + memory-copy traces of a --stacks-only run")
     ap.add_argument("--stacks-only", action="store_true",
                     help="only the two whole streamed stacks (for traces of the streaming)")
+    ap.add_argument("--micro", action="store_true",
+                    help="only the microbenchmarks that set the roofline denominators")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 256 MiB device-to-device copies (counter scale reference)")
     args = ap.parse_args()
@@ -350,118 +587,46 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_launch": src.numel() * 4, "launches": 5}))
         return 0
+    if args.micro:
+        print(json.dumps({"micro": micro_leg(torch, dev)}), flush=True)
+        return 0
     if args.stacks_only:
         out = {key: stack_leg(mp, wl, torch, dev, key, args.stack_passes) for key in STACK_KEYS}
         print(json.dumps({"stacks": out}), flush=True)
         return 0
-    w = wl.WORKLOADS["resident"]
-    T, d, f, E, k = w.T, w.d, w.f, w.E, w.k
-    R = T * k
-    log(f"[bench] {w.name}: generating inputs")
-    x = torch.from_numpy(wl.layer_activations(w, 0)).to(dev)
-    lg = torch.from_numpy(wl.layer_logits(w, 0)).to(dev)
-    blob_h = torch.empty(mp.moe_prefill_layer_bytes(d, f, E), dtype=torch.uint8)
-    mp.pack_layer(d, f, E, lambda e: wl.expert_weights(w, 0, e), blob_h)
-    blob = blob_h.to(dev)
-    y = torch.empty(T, d, device=dev)
-    h = mp.moe_prefill_create(d, f, E, k, T, device=0)
-    stream = torch.cuda.current_stream(dev)
+    # ---- measured denominators first (this also brings the clocks to their loaded state)
+    micro = None
+    if not args.no_micro:
+        micro = micro_leg(torch, dev)
+        log(f"[bench] micro: int8 MFMA {micro['int8_mfma_peak_TOPS_measured']} TOPS, epilogue ceiling "
+            f"{micro['epilogue_ceiling_TOPS']} TOPS ({micro['epilogue_ceiling_form']}), copy {micro['copy_GBs']} GB/s")
 
-    def step():
-        mp.moe_prefill_run_layer(h, x, lg, y, layer=-1, weights=blob, stream=stream)
+    # ---- headline: the largest single-GPU configuration, one resident layer of the skewed
+    # 8-layer stack's shape (T=8192, d_model=4096, d_ff=1536, E=256, top-8, Zipf routing)
+    head = resident_leg(mp, wl, torch, dev, "skew", args.steps, args.warmup, micro)
+    w = wl.WORKLOADS["skew"]
+    log(f"[bench] headline {w.name}: {head['us_per_layer']:.1f} us/layer -> "
+        f"{head['tokens_per_s_per_layer']:,.0f} tokens/s per layer; gate/up GEMM "
+        f"{head['roofline']['achieved']} TOPS = {100 * head['roofline']['frac']:.2f}% of int8 peak")
 
-    # ---- headline: K whole layers, inputs resident in HBM
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    value = T / (ms_step * 1e-3)
-    log(f"[bench] {ms_step * 1e3:.1f} us/layer -> {value:,.0f} tokens/s per layer")
-
-    # ---- the same layer captured once in a HIP graph and replayed (inputs already in place)
-    graph = None
-    try:
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            mp.moe_prefill_run_layer(h, x, lg, y, layer=-1, weights=blob, stream=side)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, capture_error_mode="thread_local"):
-            mp.moe_prefill_run_layer(h, x, lg, y, layer=-1, weights=blob)
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            g.replay()
-        torch.cuda.synchronize()
-        us_graph = (time.perf_counter() - t0) * 1e6 / args.steps
-        graph = {"us_per_layer": round(us_graph, 2), "tokens_per_s_per_layer": round(T / (us_graph * 1e-6), 1)}
-        log(f"[bench] graph replay: {us_graph:.1f} us/layer")
-        del g
-    except Exception as ex:          # reported, never fatal: the direct path is the headline
-        graph = {"error": str(ex)[:200]}
-        log(f"[bench] graph capture failed: {ex}")
-
-    # ---- per-kernel device times (HIP events between the kernels, launch stream)
-    mp.moe_prefill_set_timing(h, True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    kt = mp.moe_prefill_kernel_times(h, reset=True)
-    mp.moe_prefill_set_timing(h, False)
-    kern_us = {n: (ms / c * 1e3 if c else None) for n, (c, ms) in kt.items()}
-    gu_us = kern_us["gemm_gate_up"]
-    dn_us = kern_us["gemm_down"]
-    ops_gu = 2.0 * R * (2 * f) * d           # int8 multiply-adds x 2, routed rows only
-    ops_dn = 2.0 * R * d * f
-    gu_tops = ops_gu / (gu_us * 1e-6) / 1e12
-    dn_tops = ops_dn / (dn_us * 1e-6) / 1e12
-    q_bytes = T * E * 4 + R * 8 + T * d * 4 + T * d + T * (d // 32) * 4   # logits, eidx+w, X, Xq, dx
-    c_bytes = R * d * 4 + R * 8 + T * d * 4
-    traffic = load_traffic("gemm_gate_up", "resident")
-    roofline = {
-        "bound": "mfma", "achieved": round(gu_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-        "frac": round(gu_tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
-        "kernel": "gemm_gate_up", "ops_per_launch": ops_gu, "mean_us": round(gu_us, 2),
-        "dtype": "int8 x int4 -> int32 blocks, fp32 epilogue",
-        "note": "gate/up GEMM with the fused SwiGLU + Q8 epilogue (writes Hq, not GU)",
-        # the per-element fp32 block epilogue (convert + fma per output and 32-block) on the VALU:
-        # lane-ops / s against 256 CU x 4 SIMD x 32 lanes x 2.4 GHz
-        "valu_epilogue_Tops": round(2.0 * R * (2 * f) * (d // 32) / (gu_us * 1e-6) / 1e12, 2),
-        "valu_peak_Tops": VALU_PEAK_TOPS,
-    }
-    kernels = {n: (round(v, 2) if v is not None else None) for n, v in kern_us.items()}
-    hbm = {
-        "route_quant_GBs": round(q_bytes / (kern_us["route_quant"] * 1e-6) / 1e9, 1),
-        "combine_GBs": round(c_bytes / (kern_us["combine"] * 1e-6) / 1e9, 1),
-        "gemm_down_TOPS": round(dn_tops, 2),
-        "peak_GBs": HBM_PEAK_GBS,
-    }
-    log(f"[bench] kernels (us): {kernels}")
-    log(f"[bench] gate/up GEMM {gu_tops:.1f} TOPS = {100 * gu_tops / INT8_PEAK_TOPS:.2f}% of int8 peak")
-    del blob
-    h.close()
-    torch.cuda.empty_cache()
+    # ---- the real-shape resident layer (T=1024, d_model=2048, d_ff=768, E=128, top-8): HBM-bound GEMMs
+    c1 = resident_leg(mp, wl, torch, dev, "resident", args.steps, args.warmup, micro, graph=True)
+    log(f"[bench] {c1['workload']}: {c1['us_per_layer']:.1f} us/layer; gate/up GEMM "
+        f"{c1['roofline']['achieved']} GB/s = {100 * c1['roofline']['frac']:.1f}% of HBM")
 
     line = {
         "metric": "MoE prefill tokens/s per layer (1 GPU); int8 MFMA %peak; H2D GB/s hidden %",
-        "value": round(value, 1), "unit": "tokens/s per layer", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "value": head["tokens_per_s_per_layer"], "unit": "tokens/s per layer", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["us_per_layer"] / 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
-        "data": "synthetic (seeded N(0,1) activations/logits, Q4 uniform int4 weights)",
-        "config": {"workload": w.name, "T": T, "d_model": d, "d_ff": f, "n_experts": E, "top_k": k,
-                   "weights": "resident in HBM", "global_batch": T, "seq_len": T, "parallelism": "none"},
-        "roofline": roofline, "kernels_us": kernels, "hbm": hbm, "graph_replay": graph,
+        "data": "synthetic (seeded N(0,1) activations, N(0,1) logits + Zipf(1.1) expert bias, "
+                "Q4 uniform int4 weights)",
+        "config": {"workload": w.name, "T": w.T, "d_model": w.d, "d_ff": w.f, "n_experts": w.E, "top_k": w.k,
+                   "weights": "resident in HBM", "global_batch": w.T, "seq_len": w.T, "parallelism": "none"},
+        "roofline": head["roofline"], "kernels_us": head["kernels_us"], "hbm": head["hbm"],
+        "gemm_down": head["gemm_down"], "denominators": micro,
+        "resident_c1": c1,
     }
-
     # ---- streamed stack: 4 layers through a 2-slot pool with depth-1 prefetch
     if not args.no_stream:
         ws = wl.WORKLOADS["stream4"]
@@ -599,24 +764,9 @@ def main() -> int:
             line["stacks"][key] = stack_leg(mp, wl, torch, dev, key, args.stack_passes)
             log(f"[bench] stack {key}: {line['stacks'][key]}")
 
-    # ---- CPU oracle on the host's cores, same resident layer (bounded: a few full layers)
+    # ---- CPU oracle on the host's cores, the headline layer on a bounded token sample
     if not args.no_cpu:
-        import oracle
-        xn = wl.layer_activations(w, 0)
-        ln = wl.layer_logits(w, 0)
-        cache = {e: wl.expert_weights(w, 0, e) for e in range(E)}    # inputs, not timed
-        times = []
-        for _ in range(args.cpu_reps):
-            t0 = time.perf_counter()
-            oracle.layer(xn, ln, k, cache.__getitem__, f)
-            times.append(time.perf_counter() - t0)
-        tc = sorted(times)[len(times) // 2]
-        line["cpu_baseline"] = {
-            "value": round(T / tc, 1), "unit": "tokens/s per layer", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"the full {w.name} layer, {args.cpu_reps} runs, median {tc:.2f} s "
-                      "(expert weights pre-generated, not timed)",
-        }
+        line["cpu_baseline"] = cpu_leg(wl, w, args.cpu_seconds)
         log(f"[bench] cpu oracle: {line['cpu_baseline']}")
 
     print(json.dumps(line), flush=True)

@@ -382,6 +382,27 @@ int moe_prefill_kernel_times(moe_prefill_t* h, moe_kernel_times_t* inout, int32_
 /* Name of kernel id (MOE_K_*), or "" for an unknown id. */
 const char* moe_prefill_kernel_name(int32_t id);
 
+/* --------------------------------------------------- exponential check --- */
+/*
+ * The kernels' own fp32 exponential, the one inside H = SwiGLU(GU) (the page
+ * #663 "What" names the H stage; silu(g) = g / (1 + exp(-g))) and the router
+ * weights (softmax over the k selected logits).  Hq codes are decided by H, so
+ * this function must give the same bits as any other implementation of the same
+ * Cody-Waite + Taylor steps; these two calls let a test compare it input by
+ * input, over any range of fp32 bit patterns.
+ *
+ * out[i] = exp(x) where x is the fp32 number whose bit pattern is first_bits + i,
+ * for i < n; first_bits + n <= 2^32.
+ *  - moe_prefill_exp_host: computed on the calling thread by the host build of
+ *    the same source; out is host memory.
+ *  - moe_prefill_exp_device: one kernel enqueued on `stream` (returns before
+ *    completion); out is device memory of n floats, owned by the caller.
+ * MOE_EINVAL for a null out with n > 0 or a range beyond 2^32 patterns;
+ * MOE_EHIP if the launch fails.
+ */
+int moe_prefill_exp_host(uint32_t first_bits, uint64_t n, float* out);
+int moe_prefill_exp_device(uint32_t first_bits, uint64_t n, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -105,6 +105,7 @@ EXPORTED_SYMBOLS = [
     "moe_prefill_plan_pool", "moe_prefill_plan_trim", "stream_pool_set_budget",
     "moe_prefill_get_stats", "moe_prefill_set_log", "moe_prefill_set_timing",
     "moe_prefill_kernel_times", "moe_prefill_kernel_name",
+    "moe_prefill_exp_host", "moe_prefill_exp_device",
 ]
 
 _lib = None
@@ -141,6 +142,8 @@ def lib():
     L.moe_prefill_kernel_times.argtypes = [_vp, ctypes.POINTER(moe_kernel_times_t), _i32]
     L.moe_prefill_kernel_name.argtypes = [_i32]
     L.moe_prefill_kernel_name.restype = ctypes.c_char_p
+    L.moe_prefill_exp_host.argtypes = [_u32, _u64, _vp]
+    L.moe_prefill_exp_device.argtypes = [_u32, _u64, _vp, _vp]
     _lib = L
     return L
 
@@ -283,12 +286,8 @@ def _dev_ptr(t: Optional[torch.Tensor], dtype, name: str, numel: Optional[int] =
     return t.data_ptr()
 
 
-def moe_prefill_run_layer(handle: Handle, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor,
-                          layer: int = -1, weights: Optional[torch.Tensor] = None,
-                          stream: Optional[torch.cuda.Stream] = None,
-                          exports: Optional[Dict[str, torch.Tensor]] = None) -> None:
-    """Enqueue one MoE prefill FFN layer on ``stream`` (default: torch's current stream)."""
-    P = handle.params
+def _layer_io(P: dict, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor, layer: int,
+              weights: Optional[torch.Tensor], exports: Optional[Dict[str, torch.Tensor]]) -> moe_layer_io_t:
     T = x.shape[0]
     io = moe_layer_io_t()
     io.struct_size = ctypes.sizeof(io)
@@ -312,6 +311,15 @@ def moe_prefill_run_layer(handle: Handle, x: torch.Tensor, logits: torch.Tensor,
         if name not in _EXPORTS:
             raise KeyError(name)
         setattr(io, name, _dev_ptr(t, dt[name], name, need[name]))
+    return io
+
+
+def moe_prefill_run_layer(handle: Handle, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor,
+                          layer: int = -1, weights: Optional[torch.Tensor] = None,
+                          stream: Optional[torch.cuda.Stream] = None,
+                          exports: Optional[Dict[str, torch.Tensor]] = None) -> None:
+    """Enqueue one MoE prefill FFN layer on ``stream`` (default: torch's current stream)."""
+    io = _layer_io(handle.params, x, logits, y, layer, weights, exports)
     s = stream if stream is not None else torch.cuda.current_stream(x.device)
     _check(lib().moe_prefill_run_layer(handle.ptr, ctypes.byref(io), _vp(s.cuda_stream)), handle.ptr)
 
@@ -416,3 +424,20 @@ def moe_prefill_kernel_times(handle: Handle, reset: bool = True) -> dict:
     t.struct_size = ctypes.sizeof(t)
     _check(lib().moe_prefill_kernel_times(handle.ptr, ctypes.byref(t), 1 if reset else 0), handle.ptr)
     return {moe_prefill_kernel_name(i): (int(t.launches[i]), float(t.total_ms[i])) for i in range(t.n_kernels)}
+
+
+def moe_prefill_exp_host(first_bits: int, out: np.ndarray) -> np.ndarray:
+    """The library's fp32 exponential (host build) of the inputs with bit patterns
+    first_bits .. first_bits + out.size - 1, written into out (float32, contiguous)."""
+    assert out.dtype == np.float32 and out.flags["C_CONTIGUOUS"]
+    _check(lib().moe_prefill_exp_host(first_bits, out.size, out.ctypes.data))
+    return out
+
+
+def moe_prefill_exp_device(first_bits: int, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """The kernels' fp32 exponential of the inputs with bit patterns first_bits ..
+    first_bits + out.numel() - 1, enqueued on `stream` into the device tensor out."""
+    assert out.dtype == torch.float32 and out.is_cuda and out.is_contiguous()
+    st = stream if stream is not None else torch.cuda.current_stream(out.device)
+    _check(lib().moe_prefill_exp_device(first_bits, out.numel(), out.data_ptr(), st.cuda_stream))
+    return out

@@ -8,6 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_prefill.so")
+MICRO_LIB = os.path.join(HERE, "libmoe_micro.so")   # measurement kernels (roofline denominators)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["moe_kernels.hip", "moe_runtime.cpp", "moe_pack.cpp", "moe_pool_plan.cpp"]
@@ -24,16 +25,21 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+def _hipcc(sources, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
+    cmd = [HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in sources] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libmoe_prefill.so")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    _hipcc(SOURCES, LIB, verbose)
+    _hipcc(["moe_micro.hip"], MICRO_LIB, verbose)
     return LIB
 
 

@@ -50,7 +50,7 @@ struct LayerLaunch {
     int32_t* rtok;
     int8_t* xq;
     float* dx;
-    float* gu;
+    float* gu;                // optional export of GU [R, 2f] (caller memory; nullptr: not written)
     int8_t* hq;
     float* dh;
     float* dm;
@@ -58,7 +58,6 @@ struct LayerLaunch {
     uint8_t* load_dst;        // layer and its pool slot (load_src null: the blob is in place)
     unsigned long long* load_stats;   // [2] experts and bytes loaded (device counters)
     float* h_out;             // optional export of H (nullptr: not written)
-    bool keep_gu;             // write GU to gu (for export)
     hipEvent_t* marks;        // optional: kNumKernels + 1 timing events (nullptr: none);
                               // marks[i] before kernel i, marks[kNumKernels] after the last
 };
@@ -74,5 +73,8 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st);
 // combine (and clear the membership mask for the next layer)
 hipError_t launch_combine(const LayerLaunch& L, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
+// the kernels' fp32 exponential over the inputs with bit patterns first .. first + n - 1
+hipError_t launch_exp_range(uint32_t first, uint64_t n, float* out, hipStream_t st);
+void exp_range_host(uint32_t first, uint64_t n, float* out);
 
 }  // namespace moe

@@ -23,46 +23,16 @@
 
 #include <type_traits>
 
-#include "moe_layout.h"
 #include "moe_kernels.h"
+#include "moe_layout.h"
+#include "moe_math.h"
 
 namespace moe {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-// ------------------------------------------------------------------ exp ---
-// fp32 exponential: Cody-Waite reduction (Cody & Waite, "Software Manual for
-// the Elementary Functions", 1980) with ln2 split into fp32 hi/lo parts, a
-// degree-7 Taylor polynomial (coefficients 1/j! rounded to fp32) in Horner
-// form, and the scale 2^n applied as two exact power-of-two factors.  Each
-// step is a single IEEE operation, so the result is reproducible bit for bit.
-__device__ __forceinline__ float pow2_exact(int n)  // n in [-126, 127]
-{
-    return __int_as_float((n + 127) << 23);
-}
-
-__device__ __forceinline__ float exp_cw(float x)
-{
-    if (x != x) return x;
-    if (x > 89.0f) return __int_as_float(0x7f800000);
-    if (x < -104.0f) return 0.0f;
-    const float n = __builtin_rintf(x * 0x1.715476p+0f);     // x * log2(e)
-    float r = __builtin_fmaf(-n, 0x1.62e430p-1f, x);          // - n * ln2_hi
-    r = __builtin_fmaf(-n, -0x1.05c610p-29f, r);              // - n * ln2_lo
-    float p = 0x1.a01a02p-13f;                                // 1/7!
-    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);                // 1/6!
-    p = __builtin_fmaf(p, r, 0x1.111112p-7f);                 // 1/5!
-    p = __builtin_fmaf(p, r, 0x1.555556p-5f);                 // 1/4!
-    p = __builtin_fmaf(p, r, 0x1.555556p-3f);                 // 1/3!
-    p = __builtin_fmaf(p, r, 0.5f);
-    p = __builtin_fmaf(p, r, 1.0f);
-    p = __builtin_fmaf(p, r, 1.0f);
-    const int ni = (int)n;
-    const int n1 = ni / 2;
-    const int n2 = ni - n1;
-    return (p * pow2_exact(n1)) * pow2_exact(n2);
-}
+// exp_cw (moe_math.h): the fp32 exponential of the SwiGLU and the router weights.
 
 // Q8 code of v given the block scale d (d > 0): rint(v / d) clamped to +-127.
 __device__ __forceinline__ int q8_code(float v, float d)
@@ -979,6 +949,30 @@ __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, int6
     if (i < n) p[i] = v;
 }
 
+// ---------------------------------------------------------- exp check ---
+// out[i] = exp_cw(the fp32 number with bit pattern first + i): lets a caller
+// compare the kernels' exponential with an independent one input by input.
+__global__ __launch_bounds__(256) void k_exp_range(uint32_t first, uint64_t n, float* __restrict__ out)
+{
+    const uint64_t stride = (uint64_t)gridDim.x * 256;
+    for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+        out[i] = exp_cw(__builtin_bit_cast(float, (uint32_t)(first + i)));
+}
+
+hipError_t launch_exp_range(uint32_t first, uint64_t n, float* out, hipStream_t st)
+{
+    if (n == 0) return hipSuccess;
+    const uint64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(k_exp_range, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, st, first, n,
+                       out);
+    return hipGetLastError();
+}
+
+void exp_range_host(uint32_t first, uint64_t n, float* out)
+{
+    for (uint64_t i = 0; i < n; ++i) out[i] = exp_cw(__builtin_bit_cast(float, (uint32_t)(first + i)));
+}
+
 // ------------------------------------------------------------- launches ---
 static inline unsigned nblk(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
 
@@ -1021,7 +1015,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     gu.tiles = L.tiles;
     gu.order = L.tile_order;                              // the down launch keeps it
     gu.ntiles = L.ntiles;
-    gu.out = L.keep_gu ? L.gu : nullptr;
+    gu.out = L.gu;
     gu.hq = L.hq;
     gu.dh = L.dh;
     gu.dh_stride = scale_stride(L.f);

@@ -83,7 +83,7 @@ MOE_HD static inline uint64_t mask_words(int E, int W) { return (uint64_t)E * W 
 
 struct WsLayout {
     uint64_t eidx, wts, mask, wprefix, counts, bounds, tiles, tile_order, ntiles, load_stats;
-    uint64_t rows, pos, rtok, xq, dx, gu, hq, dh, dm;
+    uint64_t rows, pos, rtok, xq, dx, hq, dh, dm;
     uint64_t total;
     int W;            // 32-token words per expert in the membership mask
     int max_tiles;    // upper bound on GEMM row tiles
@@ -112,7 +112,6 @@ static inline WsLayout ws_layout(int d, int f, int E, int k, int Tmax)
     L.rtok = take(R * 4);
     L.xq = take((uint64_t)Tmax * d);
     L.dx = take((uint64_t)Tmax * scale_stride(d) * 4);   // [Tmax][scale_stride(d)]
-    L.gu = take(R * 2 * f * 4);
     L.hq = take(R * f);
     L.dh = take(R * scale_stride(f) * 4);                 // [R][scale_stride(f)]
     L.dm = take(R * d * 4);

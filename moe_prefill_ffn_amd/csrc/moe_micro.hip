@@ -1,0 +1,325 @@
+// Microbenchmarks that set the roofline denominators of the grouped GEMMs and
+// the memory-bound kernels on the MI355X (gfx950).  Built into libmoe_micro.so,
+// a measurement library beside the product library; nothing in the layer path
+// calls it.
+//
+// The grouped GEMMs scale every 32-block's exact int32 dot product by its own
+// pair of block scales (Q8 activation scale x fp16 weight scale) and add it into
+// an fp32 accumulator in block order.  Per output element and 32-block that is
+// one int8 MFMA share (32 MACs), one scale product, one int -> float conversion
+// and one fused multiply-add.  The register-only loops below time exactly that
+// per-block arithmetic with no memory traffic, in the forms the GEMM can take:
+//
+//   mfma_i8          int8 MFMAs only (v_mfma_i32_32x32x32_i8): the matrix peak
+//   cvt_fma_mscale   scale products on the fp32 matrix cores (one
+//                    v_mfma_f32_32x32x1_2b_f32 per block for 64 rows), then a
+//                    v_cvt_f32_i32 + v_fma_f32 per element
+//   cvt_fma_vscale   scale products as one v_mul_f32 per element
+//   sub_fma_vscale   the int8 MFMA's C operand seeded with the bits of 1.5*2^23:
+//                    the result read as fp32 is 1.5*2^23 + isum exactly
+//                    (|isum| < 2^22), so one v_sub_f32 replaces the conversion
+//   sub_fma_mscale   the same with the scale products on the matrix cores
+//   valu_fma / valu_cvt / valu_sub   one VALU instruction kind alone
+//   overlap_indep    two int8 MFMAs and 64 fmas that do not depend on them: how much
+//                    of the VALU work the matrix cores can run beside
+//   pipe_cvt_fma     cvt_fma_mscale with the epilogue one block behind the MFMAs
+//                    (the MFMAs of block b+1 issue before the VALU work of block b)
+//
+// Each loop iteration is one 32-block of a 64-row x 32-column wave tile: two
+// int8 MFMAs (64 x 32 x 32 MACs) and the epilogue of its 2048 elements (32 per
+// lane).  Four workgroups of four waves per CU put four waves on every SIMD.
+// Cycle counts come from the shader clock (s_memtime) around each wave's loop.
+//
+// copy: a float4 grid-stride device copy (HBM read + write).
+// atomic: fp32 atomic adds without return into rows scattered like the
+// combine's destinations (an upper bound on a scatter-add combine's rate).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v32f __attribute__((ext_vector_type(32)));
+
+namespace {
+
+constexpr float kMagic = 12582912.0f;      // 1.5 * 2^23
+constexpr int kMagicBits = 0x4B400000;
+
+struct MicroOut {
+    unsigned long long cycles;   // summed over waves
+    unsigned long long rt;       // summed realtime ticks (100 MHz) over waves
+    float sink;
+};
+
+__device__ __forceinline__ void touch(v4i& a) { asm volatile("" : "+v"(a)); }
+__device__ __forceinline__ void touchf(float& a) { asm volatile("" : "+v"(a)); }
+
+__device__ __forceinline__ void record(MicroOut* out, unsigned long long c0, unsigned long long r0, float s)
+{
+    const unsigned long long c1 = clock64();
+    const unsigned long long r1 = wall_clock64();
+    if ((threadIdx.x & 63) == 0) {
+        atomicAdd(&out->cycles, c1 - c0);
+        atomicAdd(&out->rt, r1 - r0);
+    }
+    if (s == 1234.5678f) out->sink = s;    // never true for the seeded inputs; keeps the work live
+}
+
+template <int kTest>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_block(int iters, int seed,
+                                                                                          MicroOut* out)
+{
+    const int lane = threadIdx.x & 63;
+    v4i a0 = {seed + lane, seed * 3, lane, 7};
+    v4i a1 = {seed - lane, lane * 5, 3, seed};
+    v4i b = {lane * 7 + 1, seed ^ lane, 11, -5};
+    float dw = 0.01f + 1e-4f * (float)lane;
+    float dxv = 0.02f + 1e-5f * (float)(seed + lane);
+    float dxr[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) dxr[i] = 0.001f * (float)(i + 1) + 1e-6f * (float)lane;
+    float acc0[16], acc1[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        acc0[i] = 0.0f;
+        acc1[i] = 0.0f;
+    }
+    v16i zero, magic;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        zero[i] = 0;
+        magic[i] = kMagicBits;
+    }
+    v32f fzero;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) fzero[i] = 0.0f;
+    v16i m0 = zero, m1 = zero, m2 = zero, m3 = zero;
+    v32f tp = fzero;
+
+    __syncthreads();
+    const unsigned long long c0 = clock64();
+    const unsigned long long r0 = wall_clock64();
+    for (int it = 0; it < iters; ++it) {
+        touch(a0);
+        touch(a1);
+        touch(b);
+        if (kTest == 0) {            // int8 MFMA only: four independent accumulation chains
+            m0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b, m0, 0, 0, 0);
+            m1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b, m1, 0, 0, 0);
+            m2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, a1, m2, 0, 0, 0);
+            m3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, a0, m3, 0, 0, 0);
+            continue;
+        }
+        if (kTest == 8) {            // MFMAs beside independent VALU work
+            m0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b, m0, 0, 0, 0);
+            m1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b, m1, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc0[i]) : "v"(dxr[i]), "v"(dw));
+                asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc1[i]) : "v"(dxr[16 + i]), "v"(dw));
+                asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc0[i]) : "v"(dxr[16 + i]), "v"(dxv));
+                asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc1[i]) : "v"(dxr[i]), "v"(dxv));
+            }
+            continue;
+        }
+        if (kTest == 9) {            // epilogue of the previous block beside this block's MFMAs
+            touchf(dxv);
+            touchf(dw);
+            const v32f tn = __builtin_amdgcn_mfma_f32_32x32x1f32(dxv, dw, fzero, 0, 0, 0);
+            const v16i n0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b, zero, 0, 0, 0);
+            const v16i n1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b, zero, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                acc0[i] = __builtin_fmaf((float)m0[i], tp[i], acc0[i]);
+                acc1[i] = __builtin_fmaf((float)m1[i], tp[16 + i], acc1[i]);
+            }
+            m0 = n0;
+            m1 = n1;
+            tp = tn;
+            continue;
+        }
+        if (kTest >= 5) {            // one VALU instruction kind alone: 64 independent ones per iteration
+            float* f0 = acc0;
+            float* f1 = acc1;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (kTest == 5) {
+                    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(f0[i]) : "v"(dxr[i]), "v"(dw));
+                    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(f1[i]) : "v"(dxr[16 + i]), "v"(dw));
+                    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(f0[i]) : "v"(dxr[16 + i]), "v"(dxv));
+                    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(f1[i]) : "v"(dxr[i]), "v"(dxv));
+                } else if (kTest == 6) {
+                    asm volatile("v_cvt_f32_i32 %0, %1" : "=v"(f0[i]) : "v"(m0[i]));
+                    asm volatile("v_cvt_f32_i32 %0, %1" : "=v"(f1[i]) : "v"(m1[i]));
+                    asm volatile("v_cvt_f32_i32 %0, %1" : "=v"(dxr[i]) : "v"(m2[i]));
+                    asm volatile("v_cvt_f32_i32 %0, %1" : "=v"(dxr[16 + i]) : "v"(m3[i]));
+                } else {
+                    asm volatile("v_sub_f32 %0, %1, %2" : "=v"(f0[i]) : "v"(m0[i]), "v"(dw));
+                    asm volatile("v_sub_f32 %0, %1, %2" : "=v"(f1[i]) : "v"(m1[i]), "v"(dw));
+                    asm volatile("v_sub_f32 %0, %1, %2" : "=v"(dxr[i]) : "v"(m2[i]), "v"(dw));
+                    asm volatile("v_sub_f32 %0, %1, %2" : "=v"(dxr[16 + i]) : "v"(m3[i]), "v"(dw));
+                }
+            }
+            continue;
+        }
+        // block epilogue forms (tests 1-4)
+        constexpr bool kSub = kTest == 3 || kTest == 4;
+        constexpr bool kMScale = kTest == 1 || kTest == 4;
+        v32f t;
+        if (kMScale) {
+            touchf(dxv);
+            touchf(dw);
+            t = __builtin_amdgcn_mfma_f32_32x32x1f32(dxv, dw, fzero, 0, 0, 0);
+        }
+        const v16i is0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b, kSub ? magic : zero, 0, 0, 0);
+        const v16i is1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b, kSub ? magic : zero, 0, 0, 0);
+        if (!kMScale) touchf(dw);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float x0 = kSub ? __int_as_float(is0[i]) - kMagic : (float)is0[i];
+            const float x1 = kSub ? __int_as_float(is1[i]) - kMagic : (float)is1[i];
+            const float s0 = kMScale ? t[i] : dxr[i] * dw;
+            const float s1 = kMScale ? t[16 + i] : dxr[16 + i] * dw;
+            acc0[i] = __builtin_fmaf(x0, s0, acc0[i]);
+            acc1[i] = __builtin_fmaf(x1, s1, acc1[i]);
+        }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc0[i] + acc1[i] + (float)(m0[i] + m1[i] + m2[i] + m3[i]) + tp[i];
+    record(out, c0, r0, s);
+}
+
+__global__ __launch_bounds__(256) void k_copy(const float4* __restrict__ src, float4* __restrict__ dst, int64_t n4)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) dst[i] = src[i];
+}
+
+// Each 64-lane group adds one 256-byte slice of a source row into destination row
+// dst_row[r]; rows are read in order and scattered by the permutation.
+__global__ __launch_bounds__(256) void k_atomic(const float* __restrict__ src, const int32_t* __restrict__ dst_row,
+                                                float* __restrict__ y, int rows, int d)
+{
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)rows * d;
+    if (gid >= total) return;
+    const int r = (int)(gid / d);
+    const int c = (int)(gid - (int64_t)r * d);
+    atomicAdd(y + (int64_t)dst_row[r] * d + c, src[gid]);   // no return value used
+}
+
+}  // namespace
+
+extern "C" {
+
+// Result of one microbenchmark launch.
+typedef struct moe_micro_result {
+    double ms;               // device time of the launch (HIP events)
+    double cycles_per_wave;  // mean shader-clock cycles of one wave's timed loop (block tests)
+    double clock_ghz;        // shader clock over that loop (cycles / realtime)
+    double work;             // block tests: int8 MACs x 2 (ops); copy / atomic: bytes moved
+} moe_micro_result_t;
+
+// test: 0 mfma_i8, 1 cvt_fma_mscale, 2 cvt_fma_vscale, 3 sub_fma_vscale, 4 sub_fma_mscale,
+// 5 valu_fma, 6 valu_cvt, 7 valu_sub, 8 overlap_indep, 9 pipe_cvt_fma.  blocks_per_cu workgroups of 256 threads on each of
+// n_cu compute units.  Returns 0 or a negative HIP error.
+int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_per_cu, moe_micro_result_t* res)
+{
+    if (!res || iters < 1 || n_cu < 1 || blocks_per_cu < 1 || test < 0 || test > 9) return -1;
+    MicroOut* d_out = nullptr;
+    hipEvent_t e0, e1;
+    if (hipMalloc(&d_out, sizeof(MicroOut)) != hipSuccess) return -2;
+    (void)hipMemset(d_out, 0, sizeof(MicroOut));
+    (void)hipEventCreate(&e0);
+    (void)hipEventCreate(&e1);
+    const dim3 grid(n_cu * blocks_per_cu), blk(256);
+    (void)hipEventRecord(e0, nullptr);
+    switch (test) {
+    case 0: hipLaunchKernelGGL(k_block<0>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 1: hipLaunchKernelGGL(k_block<1>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 2: hipLaunchKernelGGL(k_block<2>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 3: hipLaunchKernelGGL(k_block<3>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 4: hipLaunchKernelGGL(k_block<4>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 5: hipLaunchKernelGGL(k_block<5>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 6: hipLaunchKernelGGL(k_block<6>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 7: hipLaunchKernelGGL(k_block<7>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 8: hipLaunchKernelGGL(k_block<8>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    default: hipLaunchKernelGGL(k_block<9>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    }
+    (void)hipEventRecord(e1, nullptr);
+    hipError_t e = hipEventSynchronize(e1);
+    MicroOut h{};
+    if (e == hipSuccess) e = hipMemcpy(&h, d_out, sizeof(MicroOut), hipMemcpyDeviceToHost);
+    float ms = 0.0f;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    (void)hipFree(d_out);
+    if (e != hipSuccess) return -3;
+    const double waves = (double)grid.x * 4.0;
+    res->ms = ms;
+    res->cycles_per_wave = (double)h.cycles / waves;
+    res->clock_ghz = h.rt ? (double)h.cycles / ((double)h.rt / 100e6) / 1e9 : 0.0;
+    // MFMA tests: MACs per iteration per wave (x2 ops); the VALU-only tests count none
+    const double macs = test == 0 ? 4.0 * 32768.0 : ((test <= 4 || test >= 8) ? 2.0 * 32768.0 : 0.0);
+    res->work = 2.0 * macs * (double)iters * waves;
+    return 0;
+}
+
+// Device copy of `bytes` (rounded down to 16) between two device buffers; reps launches,
+// ms = mean per launch.
+int moe_micro_copy(void* dst, const void* src, uint64_t bytes, int32_t grid, int32_t reps, moe_micro_result_t* res)
+{
+    if (!res || !dst || !src || reps < 1 || grid < 1) return -1;
+    hipEvent_t e0, e1;
+    (void)hipEventCreate(&e0);
+    (void)hipEventCreate(&e1);
+    const int64_t n4 = (int64_t)(bytes / 16);
+    hipLaunchKernelGGL(k_copy, dim3(grid), dim3(256), 0, nullptr, (const float4*)src, (float4*)dst, n4);
+    (void)hipEventRecord(e0, nullptr);
+    for (int i = 0; i < reps; ++i)
+        hipLaunchKernelGGL(k_copy, dim3(grid), dim3(256), 0, nullptr, (const float4*)src, (float4*)dst, n4);
+    (void)hipEventRecord(e1, nullptr);
+    const hipError_t e = hipEventSynchronize(e1);
+    float ms = 0.0f;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (e != hipSuccess) return -3;
+    res->ms = ms / reps;
+    res->cycles_per_wave = 0.0;
+    res->clock_ghz = 0.0;
+    res->work = 2.0 * (double)(n4 * 16);
+    return 0;
+}
+
+// fp32 atomic adds (no return) of src [rows, d] into y [*, d] at rows dst_row[r]; reps
+// launches, ms = mean per launch; work = bytes of src read + 4 bytes per atomic.
+int moe_micro_atomic(const float* src, const int32_t* dst_row, float* y, int32_t rows, int32_t d, int32_t reps,
+                     moe_micro_result_t* res)
+{
+    if (!res || !src || !dst_row || !y || rows < 1 || d < 1 || reps < 1) return -1;
+    hipEvent_t e0, e1;
+    (void)hipEventCreate(&e0);
+    (void)hipEventCreate(&e1);
+    const int64_t total = (int64_t)rows * d;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    hipLaunchKernelGGL(k_atomic, grid, dim3(256), 0, nullptr, src, dst_row, y, rows, d);
+    (void)hipEventRecord(e0, nullptr);
+    for (int i = 0; i < reps; ++i) hipLaunchKernelGGL(k_atomic, grid, dim3(256), 0, nullptr, src, dst_row, y, rows, d);
+    (void)hipEventRecord(e1, nullptr);
+    const hipError_t e = hipEventSynchronize(e1);
+    float ms = 0.0f;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (e != hipSuccess) return -3;
+    res->ms = ms / reps;
+    res->cycles_per_wave = 0.0;
+    res->clock_ghz = 0.0;
+    res->work = 8.0 * (double)total;
+    return 0;
+}
+
+}  // extern "C"

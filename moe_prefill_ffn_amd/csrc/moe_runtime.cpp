@@ -235,6 +235,72 @@ bool dims_ok(const moe_prefill_params_t& p, std::string* why)
     return true;
 }
 
+// Workspace pointers of one layer launch (ws: the workspace base, L its layout).
+void bind_layer(LayerLaunch& LL, uint8_t* w, const WsLayout& L, const BlobLayout& B)
+{
+    LL.W = L.W;
+    LL.load_stats = reinterpret_cast<unsigned long long*>(w + L.load_stats);
+    LL.expert_stride = B.expert_bytes;
+    LL.gu_q_off = B.gu_q;
+    LL.gu_s_off = B.gu_s;
+    LL.d_q_off = B.d_q;
+    LL.d_s_off = B.d_s;
+    LL.eidx = reinterpret_cast<int32_t*>(w + L.eidx);
+    LL.wts = reinterpret_cast<float*>(w + L.wts);
+    LL.mask = reinterpret_cast<uint32_t*>(w + L.mask);
+    LL.wprefix = reinterpret_cast<int32_t*>(w + L.wprefix);
+    LL.counts = reinterpret_cast<int32_t*>(w + L.counts);
+    LL.bounds = reinterpret_cast<int32_t*>(w + L.bounds);
+    LL.tiles = reinterpret_cast<int32_t*>(w + L.tiles);
+    LL.tile_order = reinterpret_cast<int32_t*>(w + L.tile_order);
+    LL.ntiles = reinterpret_cast<int32_t*>(w + L.ntiles);
+    LL.rows = reinterpret_cast<int32_t*>(w + L.rows);
+    LL.pos = reinterpret_cast<int32_t*>(w + L.pos);
+    LL.rtok = reinterpret_cast<int32_t*>(w + L.rtok);
+    LL.xq = reinterpret_cast<int8_t*>(w + L.xq);
+    LL.dx = reinterpret_cast<float*>(w + L.dx);
+    LL.hq = reinterpret_cast<int8_t*>(w + L.hq);
+    LL.dh = reinterpret_cast<float*>(w + L.dh);
+    LL.dm = reinterpret_cast<float*>(w + L.dm);
+}
+
+// Stream-ordered copies of the requested intermediate buffers out of the workspace.
+// (rows x row_bytes, read with a source row stride of src_pitch bytes: the block-scale
+// arrays are kept with a padded row stride in the workspace.)  GU is not here: the
+// gate/up GEMM writes it straight into the caller's buffer.
+hipError_t export_copies(const moe_layer_io_t& io, const uint8_t* ws, const WsLayout& L, int T, int d, int f,
+                         int E, int k, hipStream_t st)
+{
+    const uint64_t R = (uint64_t)T * k;
+    struct Ex {
+        void* dst;
+        uint64_t off, rows, row_bytes, src_pitch;
+    } ex[] = {
+        {io.eidx, L.eidx, 1, R * 4, R * 4},
+        {io.weights, L.wts, 1, R * 4, R * 4},
+        {io.counts, L.counts, 1, (uint64_t)E * 4, (uint64_t)E * 4},
+        {io.bounds, L.bounds, 1, (uint64_t)(E + 1) * 4, (uint64_t)(E + 1) * 4},
+        {io.rows, L.rows, 1, R * 4, R * 4},
+        {io.pos, L.pos, 1, R * 4, R * 4},
+        {io.xq, L.xq, 1, (uint64_t)T * d, (uint64_t)T * d},
+        {io.dx, L.dx, (uint64_t)T, (uint64_t)(d / 32) * 4, (uint64_t)scale_stride(d) * 4},
+        {io.hq, L.hq, 1, R * f, R * f},
+        {io.dh, L.dh, R, (uint64_t)(f / 32) * 4, (uint64_t)scale_stride(f) * 4},
+        {io.dm, L.dm, 1, R * d * 4, R * d * 4},
+    };
+    for (const Ex& x : ex) {
+        if (!x.dst || x.rows == 0) continue;
+        hipError_t e;
+        if (x.rows == 1 || x.row_bytes == x.src_pitch)
+            e = hipMemcpyAsync(x.dst, ws + x.off, x.rows * x.row_bytes, hipMemcpyDeviceToDevice, st);
+        else
+            e = hipMemcpy2DAsync(x.dst, x.row_bytes, ws + x.off, x.src_pitch, x.row_bytes, x.rows,
+                                 hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // --------------------------------------------------------------- pool ops ---
 
 // Layers of the prefetch window after `cur`: the next `depth` streamed layers
@@ -694,46 +760,21 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
         h->mask_dirty = false;
     }
 
-    uint8_t* w = h->ws;
     LayerLaunch LL;
     LL.T = T;
     LL.d = h->d;
     LL.f = h->f;
     LL.E = h->E;
     LL.k = h->k;
-    LL.W = h->L.W;
     LL.x = io.x;
     LL.logits = io.logits;
     LL.y = io.y;
     LL.blob = blob;
     LL.load_src = sparse_slot >= 0 ? h->blobs_dev[io.layer] : nullptr;
     LL.load_dst = sparse_slot >= 0 ? h->pool + (uint64_t)sparse_slot * h->slot_bytes : nullptr;
-    LL.load_stats = reinterpret_cast<unsigned long long*>(w + h->L.load_stats);
-    LL.expert_stride = h->B.expert_bytes;
-    LL.gu_q_off = h->B.gu_q;
-    LL.gu_s_off = h->B.gu_s;
-    LL.d_q_off = h->B.d_q;
-    LL.d_s_off = h->B.d_s;
-    LL.eidx = reinterpret_cast<int32_t*>(w + h->L.eidx);
-    LL.wts = reinterpret_cast<float*>(w + h->L.wts);
-    LL.mask = reinterpret_cast<uint32_t*>(w + h->L.mask);
-    LL.wprefix = reinterpret_cast<int32_t*>(w + h->L.wprefix);
-    LL.counts = reinterpret_cast<int32_t*>(w + h->L.counts);
-    LL.bounds = reinterpret_cast<int32_t*>(w + h->L.bounds);
-    LL.tiles = reinterpret_cast<int32_t*>(w + h->L.tiles);
-    LL.tile_order = reinterpret_cast<int32_t*>(w + h->L.tile_order);
-    LL.ntiles = reinterpret_cast<int32_t*>(w + h->L.ntiles);
-    LL.rows = reinterpret_cast<int32_t*>(w + h->L.rows);
-    LL.pos = reinterpret_cast<int32_t*>(w + h->L.pos);
-    LL.rtok = reinterpret_cast<int32_t*>(w + h->L.rtok);
-    LL.xq = reinterpret_cast<int8_t*>(w + h->L.xq);
-    LL.dx = reinterpret_cast<float*>(w + h->L.dx);
-    LL.gu = reinterpret_cast<float*>(w + h->L.gu);
-    LL.hq = reinterpret_cast<int8_t*>(w + h->L.hq);
-    LL.dh = reinterpret_cast<float*>(w + h->L.dh);
-    LL.dm = reinterpret_cast<float*>(w + h->L.dm);
+    bind_layer(LL, h->ws, h->L, h->B);
     LL.h_out = io.h;
-    LL.keep_gu = io.gu != nullptr;
+    LL.gu = io.gu;
     LL.marks = nullptr;
     std::array<hipEvent_t, kNumKernels + 1> tset{};
     if (h->timing) {
@@ -775,36 +816,8 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
         h->t_pending.push_back(tl);
     }
 
-    // optional exports of the intermediate buffers
-    const uint64_t R = (uint64_t)T * h->k;
-    // (rows x row_bytes, read with a source row stride of src_pitch bytes: the
-    // block-scale arrays are kept with a padded row stride in the workspace)
-    struct Ex {
-        void* dst;
-        uint64_t off, rows, row_bytes, src_pitch;
-    } ex[] = {
-        {io.eidx, h->L.eidx, 1, R * 4, R * 4},
-        {io.weights, h->L.wts, 1, R * 4, R * 4},
-        {io.counts, h->L.counts, 1, (uint64_t)h->E * 4, (uint64_t)h->E * 4},
-        {io.bounds, h->L.bounds, 1, (uint64_t)(h->E + 1) * 4, (uint64_t)(h->E + 1) * 4},
-        {io.rows, h->L.rows, 1, R * 4, R * 4},
-        {io.pos, h->L.pos, 1, R * 4, R * 4},
-        {io.xq, h->L.xq, 1, (uint64_t)T * h->d, (uint64_t)T * h->d},
-        {io.dx, h->L.dx, (uint64_t)T, (uint64_t)(h->d / 32) * 4, (uint64_t)scale_stride(h->d) * 4},
-        {io.gu, h->L.gu, 1, R * 2 * h->f * 4, R * 2 * h->f * 4},
-        {io.hq, h->L.hq, 1, R * h->f, R * h->f},
-        {io.dh, h->L.dh, R, (uint64_t)(h->f / 32) * 4, (uint64_t)scale_stride(h->f) * 4},
-        {io.dm, h->L.dm, 1, R * h->d * 4, R * h->d * 4},
-    };
-    for (const Ex& x : ex) {
-        if (!x.dst || x.rows == 0) continue;
-        if (x.rows == 1 || x.row_bytes == x.src_pitch)
-            e = hipMemcpyAsync(x.dst, h->ws + x.off, x.rows * x.row_bytes, hipMemcpyDeviceToDevice, st);
-        else
-            e = hipMemcpy2DAsync(x.dst, x.row_bytes, h->ws + x.off, x.src_pitch, x.row_bytes, x.rows,
-                                 hipMemcpyDeviceToDevice, st);
-        if (e != hipSuccess) return hip_fail(h, e, "export copy");
-    }
+    e = export_copies(io, h->ws, h->L, T, h->d, h->f, h->E, h->k, st);
+    if (e != hipSuccess) return hip_fail(h, e, "export copy");
     h->stats.layers_run++;
 
     // lookahead: queue the next streamed layers behind this one
@@ -1130,6 +1143,23 @@ int moe_prefill_kernel_times(moe_prefill_t* h, moe_kernel_times_t* inout, int32_
         }
     }
     write_struct(inout, out);
+    return MOE_OK;
+}
+
+int moe_prefill_exp_host(uint32_t first_bits, uint64_t n, float* out)
+{
+    if (n > 0 && !out) return fail(nullptr, MOE_EINVAL, "exp_host: null output");
+    if ((uint64_t)first_bits + n > (1ull << 32)) return fail(nullptr, MOE_EINVAL, "exp_host: range beyond 2^32 patterns");
+    exp_range_host(first_bits, n, out);
+    return MOE_OK;
+}
+
+int moe_prefill_exp_device(uint32_t first_bits, uint64_t n, float* out, void* stream)
+{
+    if (n > 0 && !out) return fail(nullptr, MOE_EINVAL, "exp_device: null output");
+    if ((uint64_t)first_bits + n > (1ull << 32)) return fail(nullptr, MOE_EINVAL, "exp_device: range beyond 2^32 patterns");
+    const hipError_t e = launch_exp_range(first_bits, n, out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(nullptr, e, "exp_device launch");
     return MOE_OK;
 }
 

@@ -189,6 +189,18 @@ def _active_experts(st, layer):
     return np.unique(top).size
 
 
+def test_stack_references_match_the_oracle(tiny5, skew4):
+    """The resident runs every streamed stack here is compared with, against the
+    oracle in full (every token of every layer): the pool tests then tie the
+    streamed outputs to the oracle, not only to the HIP path itself."""
+    for st in (tiny5, skew4):
+        for l in range(st.n):
+            say(f"[case] {st.w.name} layer {l} against the oracle")
+            ref = oracle.layer(wl.layer_activations(st.w, l), wl.layer_logits(st.w, l), st.w.k,
+                               ExpertCache(st.w, l), st.w.f)
+            assert_close(f"{st.w.name} layer {l} y", st.ref[l], ref["y"])
+
+
 def test_active_only_loads_only_routed_experts(skew4):
     h = make_handle(skew4.w)
     plan = _configure(h, skew4, prefetch_depth=2, resident_layers=0, requested_slots=2, active_only=True)
