@@ -170,6 +170,32 @@ typedef struct moe_layer_io {
  */
 int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io, void* stream);
 
+/*
+ * Allocation-free variant of moe_prefill_run_layer, for callers that cannot
+ * allocate device memory: code running under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It needs no handle and calls no
+ * hipMalloc, hipFree or allocating library routine.
+ *
+ *  - p: the dimensions (d_model, d_ff, n_experts, top_k, device) with the same
+ *    limits as moe_prefill_create; max_tokens is ignored (the workspace is laid
+ *    out for io->n_tokens) and workspace must be NULL.
+ *  - io: as for moe_prefill_run_layer, resident weights only (layer == -1,
+ *    weights_dev set); the optional exports work as there.
+ *  - The workspace is a static device array of 128 MiB (134217728 bytes) per
+ *    device, 256-byte aligned, that the library holds until the process ends.
+ *    A layer whose workspace (moe_prefill_workspace_size with max_tokens =
+ *    n_tokens) is larger is refused with MOE_EINVAL before anything is enqueued
+ *    (e.g. d_model=2048, d_ff=768, 128 experts, top-8 fits up to ~1700 tokens).
+ *  - Every call on a device shares that device's array, which keeps the last
+ *    call's contents; each call first clears, with a kernel on `stream`, the
+ *    parts that must start at zero.  Calls that overlap on one device (other
+ *    streams, other threads) race on the array: the caller serialises them.
+ *  - Work is enqueued on `stream` and the call returns before completion.
+ * Errors: MOE_EINVAL (bad dimensions, pointers, too large a layer),
+ * MOE_EUNSUPPORTED (not gfx950), MOE_EHIP.
+ */
+int moe_prefill_run_layer_noalloc(const moe_prefill_params_t* p, const moe_layer_io_t* io, void* stream);
+
 /* ---------------------------------------------------------- stream pool --- */
 
 typedef struct stream_pool_params {

@@ -105,7 +105,7 @@ EXPORTED_SYMBOLS = [
     "moe_prefill_plan_pool", "moe_prefill_plan_trim", "stream_pool_set_budget",
     "moe_prefill_get_stats", "moe_prefill_set_log", "moe_prefill_set_timing",
     "moe_prefill_kernel_times", "moe_prefill_kernel_name",
-    "moe_prefill_exp_host", "moe_prefill_exp_device",
+    "moe_prefill_exp_host", "moe_prefill_exp_device", "moe_prefill_run_layer_noalloc",
 ]
 
 _lib = None
@@ -142,6 +142,8 @@ def lib():
     L.moe_prefill_kernel_times.argtypes = [_vp, ctypes.POINTER(moe_kernel_times_t), _i32]
     L.moe_prefill_kernel_name.argtypes = [_i32]
     L.moe_prefill_kernel_name.restype = ctypes.c_char_p
+    L.moe_prefill_run_layer_noalloc.argtypes = [ctypes.POINTER(moe_prefill_params_t),
+                                                ctypes.POINTER(moe_layer_io_t), _vp]
     L.moe_prefill_exp_host.argtypes = [_u32, _u64, _vp]
     L.moe_prefill_exp_device.argtypes = [_u32, _u64, _vp, _vp]
     _lib = L
@@ -322,6 +324,20 @@ def moe_prefill_run_layer(handle: Handle, x: torch.Tensor, logits: torch.Tensor,
     io = _layer_io(handle.params, x, logits, y, layer, weights, exports)
     s = stream if stream is not None else torch.cuda.current_stream(x.device)
     _check(lib().moe_prefill_run_layer(handle.ptr, ctypes.byref(io), _vp(s.cuda_stream)), handle.ptr)
+
+
+def moe_prefill_run_layer_noalloc(d_model: int, d_ff: int, n_experts: int, top_k: int, x: torch.Tensor,
+                                  logits: torch.Tensor, y: torch.Tensor, weights: torch.Tensor,
+                                  device: int = 0, stream: Optional[torch.cuda.Stream] = None,
+                                  exports: Optional[Dict[str, torch.Tensor]] = None) -> None:
+    """One resident layer with no handle and no device allocation: the library's static
+    per-device scratch array is the workspace (calls on one device must not overlap)."""
+    T = x.shape[0]
+    P = dict(d_model=d_model, d_ff=d_ff, n_experts=n_experts, top_k=top_k, max_tokens=max(T, 1))
+    io = _layer_io(P, x, logits, y, -1, weights, exports)
+    p = _params(d_model, d_ff, n_experts, top_k, max(T, 1), device)
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    _check(lib().moe_prefill_run_layer_noalloc(ctypes.byref(p), ctypes.byref(io), _vp(s.cuda_stream)))
 
 
 # ----------------------------------------------------------- stream pool ---

@@ -73,6 +73,10 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st);
 // combine (and clear the membership mask for the next layer)
 hipError_t launch_combine(const LayerLaunch& L, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
+// Device address of the static scratch array of device `dev` (which must be current);
+// looked up once per device.  kScratchBytes bytes, 256-byte aligned.
+constexpr uint64_t kScratchBytes = 128ull << 20;
+hipError_t scratch_device_ptr(int dev, uint8_t** out);
 // the kernels' fp32 exponential over the inputs with bit patterns first .. first + n - 1
 hipError_t launch_exp_range(uint32_t first, uint64_t n, float* out, hipStream_t st);
 void exp_range_host(uint32_t first, uint64_t n, float* out);

@@ -21,6 +21,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "moe_kernels.h"
@@ -971,6 +972,33 @@ hipError_t launch_exp_range(uint32_t first, uint64_t n, float* out, hipStream_t 
 void exp_range_host(uint32_t first, uint64_t n, float* out)
 {
     for (uint64_t i = 0; i < n; ++i) out[i] = exp_cw(__builtin_bit_cast(float, (uint32_t)(first + i)));
+}
+
+// ------------------------------------------------------- static scratch ---
+// Workspace of the allocation-free layer entry point: one array per device, held
+// until the process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address comes from hipGetSymbolAddress, once per device
+// with that device current, and only that address is ever handed to a kernel or a
+// copy.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kScratchMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static uint8_t* g_scratch_ptr[kScratchMaxDevices] = {};
+
+hipError_t scratch_device_ptr(int dev, uint8_t** out)
+{
+    *out = nullptr;
+    if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;                                   // the caller made `dev` current
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 // ------------------------------------------------------------- launches ---

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <array>
 #include <chrono>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -299,6 +300,26 @@ hipError_t export_copies(const moe_layer_io_t& io, const uint8_t* ws, const WsLa
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// The allocation-free entry point's device check (gfx950), once per device.
+int noalloc_device_ok(int dev)
+{
+    static std::mutex mu;
+    static std::vector<signed char> ok;                  // -1 unknown, 0 refused, 1 accepted
+    std::lock_guard<std::mutex> lock(mu);
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(nullptr, MOE_EUNSUPPORTED, "no HIP device");
+    if (dev < 0 || dev >= ndev) return fail(nullptr, MOE_EINVAL, "device ordinal out of range");
+    if ((int)ok.size() < ndev) ok.resize(ndev, -1);
+    if (ok[dev] < 0) {
+        hipDeviceProp_t prop;
+        const hipError_t e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(nullptr, e, "hipGetDeviceProperties");
+        ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    }
+    if (!ok[dev]) return fail(nullptr, MOE_EUNSUPPORTED, "device is not gfx950");
+    return MOE_OK;
 }
 
 // --------------------------------------------------------------- pool ops ---
@@ -844,6 +865,68 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
         }
     }
     h->err.clear();
+    return MOE_OK;
+}
+
+int moe_prefill_run_layer_noalloc(const moe_prefill_params_t* pin, const moe_layer_io_t* io_in, void* stream)
+{
+    moe_prefill_params_t p;
+    moe_layer_io_t io;
+    std::string why;
+    if (!read_struct(pin, &p, &why)) return fail(nullptr, MOE_EINVAL, why);
+    if (!read_struct(io_in, &io, &why)) return fail(nullptr, MOE_EINVAL, why);
+    const int T = io.n_tokens;
+    if (T < 0) return fail(nullptr, MOE_EINVAL, "noalloc: n_tokens < 0");
+    p.max_tokens = T > 0 ? T : 1;                     // the workspace is laid out for this T
+    if (!dims_ok(p, &why)) return fail(nullptr, MOE_EINVAL, why);
+    if (p.workspace) return fail(nullptr, MOE_EINVAL, "noalloc: workspace must be NULL (the static scratch is the workspace)");
+    if (T == 0) return MOE_OK;
+    if (io.layer != -1 || !io.weights_dev)
+        return fail(nullptr, MOE_EINVAL, "noalloc: resident weights only (layer = -1 and weights_dev)");
+    if (!io.x || !io.logits || !io.y) return fail(nullptr, MOE_EINVAL, "x, logits and y are required");
+    if ((reinterpret_cast<uintptr_t>(io.x) | reinterpret_cast<uintptr_t>(io.y) |
+         reinterpret_cast<uintptr_t>(io.h)) % 16)
+        return fail(nullptr, MOE_EINVAL, "x, y and h must be 16-byte aligned");
+    const WsLayout L = ws_layout(p.d_model, p.d_ff, p.n_experts, p.top_k, T);
+    if (L.total > kScratchBytes)
+        return fail(nullptr, MOE_EINVAL, "noalloc: this layer needs " + std::to_string(L.total) +
+                    " bytes of workspace, more than the static scratch of " + std::to_string(kScratchBytes) +
+                    " bytes; use moe_prefill_run_layer");
+    const int rc = noalloc_device_ok(p.device);
+    if (rc != MOE_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    DevGuard guard(p.device);
+    uint8_t* ws = nullptr;
+    hipError_t e = scratch_device_ptr(p.device, &ws);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "noalloc: static scratch address");
+    // The membership mask and the scale flags must start at zero.  Their place in the
+    // scratch depends on the dimensions and an earlier call may have left other data
+    // there, so every call clears them (a kernel, not a memset: safe to capture).
+    e = launch_fill_u32(reinterpret_cast<uint32_t*>(ws + L.mask), (int64_t)mask_words(p.n_experts, L.W), 0u, st);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "noalloc: grouping state reset");
+    const BlobLayout B = blob_layout(p.d_model, p.d_ff);
+    LayerLaunch LL;
+    LL.T = T;
+    LL.d = p.d_model;
+    LL.f = p.d_ff;
+    LL.E = p.n_experts;
+    LL.k = p.top_k;
+    LL.x = io.x;
+    LL.logits = io.logits;
+    LL.y = io.y;
+    LL.blob = static_cast<const uint8_t*>(io.weights_dev);
+    LL.load_src = nullptr;
+    LL.load_dst = nullptr;
+    bind_layer(LL, ws, L, B);
+    LL.h_out = io.h;
+    LL.gu = io.gu;
+    LL.marks = nullptr;
+    e = launch_layer(LL, st);
+    if (e == hipSuccess) e = launch_combine(LL, st);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "noalloc: layer launch");
+    e = export_copies(io, ws, L, T, p.d_model, p.d_ff, p.n_experts, p.top_k, st);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "noalloc: export copy");
+    g_err.clear();
     return MOE_OK;
 }
 
