@@ -517,6 +517,11 @@ def micro_leg(torch, dev) -> dict:
         r = micro.block(name, iters, n_cu, 4)
         valu[name] = round(r["cycles_per_wave"] / (4 * 64 * iters), 3)   # SIMD cycles per wave64 instruction
     out["valu_cycles_per_wave_instr"] = valu
+    iters = 20000
+    r = micro.block("mfma_f32_scale", iters, n_cu, 4)
+    # SIMD cycles per scale-product MFMA (4 waves per SIMD, 2 per iteration) and products/s
+    out["mfma_f32_scale"] = {"cycles_per_instr": round(r["cycles_per_wave"] / (4 * 2 * iters), 2),
+                             "G_products_per_s": round(r["work"] / 2 / (r["ms"] * 1e-3) / 1e9, 1)}
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)

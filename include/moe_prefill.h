@@ -70,10 +70,10 @@ typedef struct moe_prefill moe_prefill_t;
 
 typedef struct moe_prefill_params {
     uint32_t struct_size;
-    int32_t d_model;          /* d: multiple of 64, 64..16384 */
-    int32_t d_ff;             /* f, per expert: multiple of 64, 64..16384 */
+    int32_t d_model;          /* d: multiple of 32 (one Q8/Q4 block), 32..16384 */
+    int32_t d_ff;             /* f, per expert: multiple of 32, 32..16384 */
     int32_t n_experts;        /* E: 1..1024 */
-    int32_t top_k;            /* k: 1..min(E, 64) */
+    int32_t top_k;            /* k: 1..E */
     int32_t max_tokens;       /* largest T any run will use: >= 1, max_tokens*top_k <= 2^21 */
     int32_t device;           /* HIP device ordinal */
     int32_t reserved0;

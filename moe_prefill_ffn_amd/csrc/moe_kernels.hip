@@ -103,19 +103,20 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
     return ((uint64_t)hi << 32) | lo;
 }
 
-// router weights of the token's k slots, whose logits are in zsel[0 .. k)
+// router weights of the token's k slots, whose logits are in zsel[0 .. k) (k <= 1024):
+// z_j = exp(l_j - l_0) (lane j % 64 computes slot j), S = z_0 + ... + z_{k-1} summed in
+// ascending slot order, w_j = z_j / S
 __device__ __forceinline__ void route_weights(int t, int k, float* __restrict__ wts, float* zsel)
 {
     const int lane = threadIdx.x & 63;
     __builtin_amdgcn_wave_barrier();
     const float top = zsel[0];
-    const float z = lane < k ? exp_cw(zsel[lane] - top) : 0.0f;
     __builtin_amdgcn_wave_barrier();
-    if (lane < k) zsel[lane] = z;
+    for (int j = lane; j < k; j += 64) zsel[j] = exp_cw(zsel[j] - top);
     __builtin_amdgcn_wave_barrier();
     float sum = 0.0f;
     for (int j = 0; j < k; ++j) sum += zsel[j];
-    if (lane < k) wts[(int64_t)t * k + lane] = z / sum;
+    for (int j = lane; j < k; j += 64) wts[(int64_t)t * k + j] = zsel[j] / sum;
 }
 
 // E <= kRankMaxE: one token per workgroup.  Thread (e = tid % 128, part = tid / 128)
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(256) void k_route_quant(const float* __restrict__ l
 {
     __shared__ uint64_t keys[kRankMaxE];
     __shared__ int prank[kRankMaxE];
-    __shared__ float zsel[4][64];
+    __shared__ float zsel[4][kRouteMaxE];                 // selected logits, then their exps
     if ((int)blockIdx.x < n_route) {
         if (E <= kRankMaxE) {                             // one token per workgroup
             const int t = blockIdx.x;
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
         int lo = lo0, r0, r1, nheavy = 0;
         for (int tau = t0; tau < t1; ++tau) {
             tile_rows(tau, lo, r0, r1);
-            nheavy += r1 - r0 > 32;
+            nheavy += r1 - r0 > kBM / 2;
         }
         int hincl = nheavy;                               // heavy tiles up to this run's end
 #pragma unroll
@@ -458,7 +459,7 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
             for (int x = 0; x < 8; ++x)
                 if (range_start(x) == tau) s_hstart[x] = h;
             tile_rows(tau, lo, r0, r1);
-            h += r1 - r0 > 32;
+            h += r1 - r0 > kBM / 2;
         }
         __syncthreads();
         lo = lo0;
@@ -467,7 +468,7 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
             int x = 7;
             while (range_start(x) > tau) --x;              // the range holding tau
             tile_rows(tau, lo, r0, r1);
-            const bool heavy = r1 - r0 > 32;
+            const bool heavy = r1 - r0 > kBM / 2;
             const int ta = range_start(x), hx = h - s_hstart[x];
             const int nh = s_hstart[x + 1] - s_hstart[x];
             tile_order[heavy ? ta + hx : ta + nh + (tau - ta - hx)] = tau;
@@ -529,11 +530,13 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
 // n-groups of a row tile and the row tiles of an expert share that XCD's L2.
 // Inside an XCD's run both launches take the tiles of more than 32 rows first,
 // so the workgroups that start last are the cheaper half-height ones.
+constexpr int kGemmThreads = 256;         // 4 waves
 constexpr int kRing = 4;                  // LDS stages = stages per scale group
 constexpr int kA_OFF = 0;                 // [64 rows][4 chunks of 16 B], chunks swizzled per row
 constexpr int kB_OFF = 4096;              // [4 waves][64 lanes][16 B]
 constexpr int kStageBytes = 8192;
 constexpr int kScaleBytes = 4096;         // [4 waves][ {32 cols x 8 fp16} | {16 rows x 8 fp32} ]
+static_assert(kBM == 64, "a tile is one 64-row block of one expert");
 static_assert(kRing * 2 == kScaleGroup, "one scale group per pass over the ring");
 
 typedef float v32f __attribute__((ext_vector_type(32)));
@@ -599,13 +602,14 @@ __device__ __forceinline__ int a_lds_off(int r, int c) { return r * 64 + ((c ^ a
 // arithmetic as the standalone SwiGLU + Q8 step.  GU and H are written out only
 // when asked for (g.out, g.h_out).
 constexpr int kXsStride = 136;            // floats per staged row (128 + 8 pad)
+constexpr int kXsBytes = kBM * kXsStride * 4;
 
 __device__ __forceinline__ void swiglu_q8_epilogue(const GemmArgs& g, uint8_t* lds,
                                                    const float (&acc0)[16], const float (&acc1)[16],
-                                                   int r0, int nrows, int ng, int nt)
+                                                   int r0, int nrows, int ng, int nt, bool wave_on)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, j32 = lane & 31;
-    if (g.out) {
+    if (g.out && wave_on) {
         const int col = gu_logical_row(nt, j32, g.gu_f);
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
@@ -628,10 +632,11 @@ __device__ __forceinline__ void swiglu_q8_epilogue(const GemmArgs& g, uint8_t* l
     __syncthreads();
     const int f = g.gu_f;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int t = it * 256 + tid;                     // (row, f-block of the pair, 4-column slice)
+    for (int it = 0; it < kBM * 16 / kGemmThreads; ++it) {
+        const int t = it * kGemmThreads + tid;            // (row, f-block of the pair, 4-column slice)
         const int row = t >> 4, fb = (t >> 3) & 1, sub = t & 7;
         if (row >= nrows) continue;                       // uniform over the 8-lane group
+        if ((2 * ng + fb) * 32 >= f) continue;            // f % 64 == 32: the last group holds one f-block
         const float* xr = xs + row * kXsStride + fb * 64 + sub * 4;
         const float4 gv = *reinterpret_cast<const float4*>(xr);
         const float4 uv = *reinterpret_cast<const float4*>(xr + 32);
@@ -693,7 +698,8 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g, const GemmI
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int K = g.K, N = g.N;
-    const int npairs = K >> 6, ngroups = scale_groups(K);
+    const int npairs = k_pairs(K), ngroups = scale_groups(K);
+    const bool half_tail = (K & 63) != 0;                 // K % 64 == 32: the last pair holds one block
     const int nt_real = ng * 4 + wave;
     const bool wave_on = nt_real < (N >> 5);
     const int nt = wave_on ? nt_real : (N >> 5) - 1;      // idle waves load valid memory
@@ -790,6 +796,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g, const GemmI
         if (U == 0) issue_scales(grp + 1, (grp + 1) & 1);
         issue_stage(s + kRing - 1, (U + kRing - 1) % kRing);
         if (!wave_on) return;
+        const bool one_block = half_tail && s == npairs - 1;   // skip the padded second block
         const uint8_t* sb = ring + U * kStageBytes;
         const uint8_t* sc = sbuf + (grp & 1) * kScaleBytes;
         const uint4 bq = *reinterpret_cast<const uint4*>(sb + kB_OFF + wave * 1024 + lane * 16);
@@ -803,6 +810,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g, const GemmI
             const v32f t = __builtin_amdgcn_mfma_f32_32x32x1f32(dxv, dw, fzero, 0, 0, 0);
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
+                if (q == 1 && one_block) break;
                 const uint32_t w0 = q ? bq.z : bq.x;
                 const uint32_t w1 = q ? bq.w : bq.y;
                 const v4i bop = unpack_b<kFold>(w0, w1);
@@ -817,6 +825,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g, const GemmI
         const float2 dx = *reinterpret_cast<const float2*>(sc + xs_off + (U >> 1) * 16 + (U & 1) * 8);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
+            if (q == 1 && one_block) break;
             const uint32_t w0 = q ? bq.z : bq.x;
             const uint32_t w1 = q ? bq.w : bq.y;
             const v4i bop = unpack_b<kFold>(w0, w1);
@@ -870,7 +879,7 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g, const GemmI
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the clamped tail loads before exit
 
     if (kGateUp) {
-        swiglu_q8_epilogue(g, lds, acc0, acc1, r0, nrows, ng, nt);
+        swiglu_q8_epilogue(g, lds, acc0, acc1, r0, nrows, ng, nt, wave_on);
         return;
     }
     if (!wave_on) return;
@@ -888,12 +897,13 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g, const GemmI
 
 // gate/up projection: A rows gathered from Xq through the row table, output
 // columns in logical gate | up order.
-constexpr int kGemmLds = kRing * kStageBytes + 2 * kScaleBytes;   // 40 KiB: four workgroups per CU
+constexpr int kGemmLdsRing = kRing * kStageBytes + 2 * kScaleBytes;
+constexpr int kGemmLds = kGemmLdsRing > kXsBytes ? kGemmLdsRing : kXsBytes;   // 40 KiB: four workgroups per CU
 
 // The launch reads the scale flag once and runs one of the two instantiations; the
 // LDS is declared here, once, so both share it (a __shared__ array inside the
 // template would be allocated per instantiation).
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_gate_up(GemmArgs g)
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_gate_up(GemmArgs g)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kGemmLds];
     GemmItem it;
@@ -904,7 +914,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         grouped_gemm_body<true, false>(g, it, lds);
 }
 // down projection: A = Hq in row-table order.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_down(GemmArgs g)
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_down(GemmArgs g)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kGemmLds];
     GemmItem it;
@@ -1056,7 +1066,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     gu.h_flag = L.mask + (int64_t)L.E * L.W + 1;           // H scales (set by this launch)
     mark(L, kGemmGateUp, st);
     const unsigned tiles8 = 8 * nblk(max_tiles_now, 8);   // every XCD's tile range, rounded up
-    hipLaunchKernelGGL(k_gemm_gate_up, dim3(nblk(gu.N / 32, 4) * tiles8), dim3(256), 0, st, gu);
+    hipLaunchKernelGGL(k_gemm_gate_up, dim3(nblk(gu.N / 32, 4) * tiles8), dim3(kGemmThreads), 0, st, gu);
 
     GemmArgs dn = gu;
     dn.A = L.hq;
@@ -1075,7 +1085,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     dn.fold_flag = gu.h_flag;
     dn.h_flag = nullptr;
     mark(L, kGemmDown, st);
-    hipLaunchKernelGGL(k_gemm_down, dim3(nblk(dn.N / 32, 4) * tiles8), dim3(256), 0, st, dn);
+    hipLaunchKernelGGL(k_gemm_down, dim3(nblk(dn.N / 32, 4) * tiles8), dim3(kGemmThreads), 0, st, dn);
     mark(L, kCombine, st);
     return hipGetLastError();
 }

@@ -23,8 +23,9 @@ MOE_HD static inline uint64_t align_up(uint64_t x, uint64_t a) { return (x + a -
 // section 256-byte aligned.  A matrix W [N, K] (N output rows, K input) is
 // stored in tiles of 32 output rows ("n-tiles") by pairs of K-blocks (64 K):
 //
-//   quants: for nt < N/32, pr < K/64, lane < 64: 16 bytes at
-//           ((nt * K/64 + pr) * 64 + lane) * 16
+//   quants: for nt < N/32, pr < ceil(K/64), lane < 64: 16 bytes at
+//           ((nt * ceil(K/64) + pr) * 64 + lane) * 16 (K % 64 == 32: the second
+//           block of the last pair holds code 8, i.e. weight 0)
 //     lane = h * 32 + j  (j: row inside the n-tile, h: which 16-K half of a block)
 //     bytes 8q .. 8q+7 hold block b = 2 pr + q, K range [32 b + 16 h, +16):
 //       byte i   (i < 4): low nibble K+i,    high nibble K+4+i
@@ -48,6 +49,9 @@ struct BlobLayout {
 
 constexpr int kScaleGroup = 8;   // K-blocks per scale group
 
+// K pairs (64 K each) of a K extent; with K % 64 == 32 the last pair holds one block
+MOE_HD static inline int k_pairs(int K) { return (K + 63) / 64; }
+
 // scale groups of a K extent, and the padded per-row stride (in blocks) of the
 // activation block-scale arrays the GEMMs read a whole group at a time from
 MOE_HD static inline int scale_groups(int K) { return (K / 32 + kScaleGroup - 1) / kScaleGroup; }
@@ -56,9 +60,9 @@ MOE_HD static inline int scale_stride(int K) { return scale_groups(K) * kScaleGr
 static inline BlobLayout blob_layout(int d, int f)
 {
     BlobLayout L;
-    uint64_t n_gu_q = (uint64_t)2 * f * d / 2;
+    uint64_t n_gu_q = (uint64_t)2 * f * k_pairs(d) * 32;
     uint64_t n_gu_s = (uint64_t)2 * f * scale_stride(d) * 2;
-    uint64_t n_d_q = (uint64_t)d * f / 2;
+    uint64_t n_d_q = (uint64_t)d * k_pairs(f) * 32;
     uint64_t n_d_s = (uint64_t)d * scale_stride(f) * 2;
     L.gu_q = 0;
     L.gu_s = L.gu_q + align_up(n_gu_q, 256);
@@ -110,9 +114,9 @@ static inline WsLayout ws_layout(int d, int f, int E, int k, int Tmax)
     L.rows = take(R * 4);
     L.pos = take(R * 4);
     L.rtok = take(R * 4);
-    L.xq = take((uint64_t)Tmax * d);
+    L.xq = take((uint64_t)Tmax * d + 64);                // + 64: a half last K pair reads past a row
     L.dx = take((uint64_t)Tmax * scale_stride(d) * 4);   // [Tmax][scale_stride(d)]
-    L.hq = take(R * f);
+    L.hq = take(R * f + 64);
     L.dh = take(R * scale_stride(f) * 4);                 // [R][scale_stride(f)]
     L.dm = take(R * d * 4);
     L.total = o;

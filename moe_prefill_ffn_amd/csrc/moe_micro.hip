@@ -22,6 +22,7 @@
 //   valu_fma / valu_cvt / valu_sub   one VALU instruction kind alone
 //   overlap_indep    two int8 MFMAs and 64 fmas that do not depend on them: how much
 //                    of the VALU work the matrix cores can run beside
+//   mfma_f32_scale   v_mfma_f32_32x32x1_2b_f32 alone (the scale-product MFMA)
 //   pipe_cvt_fma     cvt_fma_mscale with the epilogue one block behind the MFMAs
 //                    (the MFMAs of block b+1 issue before the VALU work of block b)
 //
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
     for (int i = 0; i < 32; ++i) fzero[i] = 0.0f;
     v16i m0 = zero, m1 = zero, m2 = zero, m3 = zero;
-    v32f tp = fzero;
+    v32f tp = fzero, t2 = fzero;
 
     __syncthreads();
     const unsigned long long c0 = clock64();
@@ -108,6 +109,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
             m1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b, m1, 0, 0, 0);
             m2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, a1, m2, 0, 0, 0);
             m3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, a0, m3, 0, 0, 0);
+            continue;
+        }
+        if (kTest == 10) {           // the fp32 scale-product MFMA alone, zero C as in the GEMM
+            touchf(dxv);
+            touchf(dw);
+            tp = __builtin_amdgcn_mfma_f32_32x32x1f32(dxv, dw, fzero, 0, 0, 0);
+            t2 = __builtin_amdgcn_mfma_f32_32x32x1f32(dw, dxv, fzero, 0, 0, 0);
+            asm volatile("" : "+v"(tp), "+v"(t2));
             continue;
         }
         if (kTest == 8) {            // MFMAs beside independent VALU work
@@ -186,7 +195,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     }
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s += acc0[i] + acc1[i] + (float)(m0[i] + m1[i] + m2[i] + m3[i]) + tp[i];
+    for (int i = 0; i < 16; ++i) s += acc0[i] + acc1[i] + (float)(m0[i] + m1[i] + m2[i] + m3[i]) + tp[i] + t2[i];
     record(out, c0, r0, s);
 }
 
@@ -222,11 +231,11 @@ typedef struct moe_micro_result {
 } moe_micro_result_t;
 
 // test: 0 mfma_i8, 1 cvt_fma_mscale, 2 cvt_fma_vscale, 3 sub_fma_vscale, 4 sub_fma_mscale,
-// 5 valu_fma, 6 valu_cvt, 7 valu_sub, 8 overlap_indep, 9 pipe_cvt_fma.  blocks_per_cu workgroups of 256 threads on each of
+// 5 valu_fma, 6 valu_cvt, 7 valu_sub, 8 overlap_indep, 9 pipe_cvt_fma, 10 mfma_f32_scale.  blocks_per_cu workgroups of 256 threads on each of
 // n_cu compute units.  Returns 0 or a negative HIP error.
 int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_per_cu, moe_micro_result_t* res)
 {
-    if (!res || iters < 1 || n_cu < 1 || blocks_per_cu < 1 || test < 0 || test > 9) return -1;
+    if (!res || iters < 1 || n_cu < 1 || blocks_per_cu < 1 || test < 0 || test > 10) return -1;
     MicroOut* d_out = nullptr;
     hipEvent_t e0, e1;
     if (hipMalloc(&d_out, sizeof(MicroOut)) != hipSuccess) return -2;
@@ -245,7 +254,8 @@ int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_pe
     case 6: hipLaunchKernelGGL(k_block<6>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     case 7: hipLaunchKernelGGL(k_block<7>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     case 8: hipLaunchKernelGGL(k_block<8>, grid, blk, 0, nullptr, iters, 3, d_out); break;
-    default: hipLaunchKernelGGL(k_block<9>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 9: hipLaunchKernelGGL(k_block<9>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    default: hipLaunchKernelGGL(k_block<10>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     }
     (void)hipEventRecord(e1, nullptr);
     hipError_t e = hipEventSynchronize(e1);
@@ -262,7 +272,11 @@ int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_pe
     res->cycles_per_wave = (double)h.cycles / waves;
     res->clock_ghz = h.rt ? (double)h.cycles / ((double)h.rt / 100e6) / 1e9 : 0.0;
     // MFMA tests: MACs per iteration per wave (x2 ops); the VALU-only tests count none
-    const double macs = test == 0 ? 4.0 * 32768.0 : ((test <= 4 || test >= 8) ? 2.0 * 32768.0 : 0.0);
+    // MFMA tests: int8 MACs per iteration per wave (x2 ops); mfma_f32_scale counts its fp32
+    // products (2 x 2048 per iteration); the VALU-only tests count none
+    const double macs = test == 0 ? 4.0 * 32768.0
+                      : test == 10 ? 2.0 * 2048.0
+                      : ((test <= 4 || test == 8 || test == 9) ? 2.0 * 32768.0 : 0.0);
     res->work = 2.0 * macs * (double)iters * waves;
     return 0;
 }

@@ -6,13 +6,14 @@
 
 namespace moe {
 
-// W [N, K] int8 in [-8, 7], S [N, K/32] fp16 bits -> quant and scale sections.
+// W [N, K] int8 in [-8, 7], S [N, K/32] fp16 bits -> quant and scale sections
+// (K a multiple of 32; with K % 64 == 32 the last K pair holds one block and zero codes).
 // interleave_f > 0: W is the gate/up matrix with f = interleave_f (blob n-tile
 // 2i = gate rows 32i.., 2i+1 = up rows f + 32i..).
 static bool pack_matrix(int N, int K, const int8_t* W, const uint16_t* S, int interleave_f,
                         uint8_t* q_dst, uint8_t* s_dst)
 {
-    const int npairs = K / 64, nbk = K / 32, ngroups = scale_groups(K);
+    const int npairs = k_pairs(K), nbk = K / 32, ngroups = scale_groups(K);
     for (int64_t i = 0; i < (int64_t)N * K; ++i)
         if (W[i] < -8 || W[i] > 7) return false;
     for (int nt = 0; nt < N / 32; ++nt) {
@@ -25,6 +26,10 @@ static bool pack_matrix(int N, int K, const int8_t* W, const uint16_t* S, int in
                 uint8_t* out = qt + lane * 16;
                 for (int q = 0; q < 2; ++q) {
                     const int k0 = 32 * (2 * pr + q) + 16 * h;
+                    if (k0 >= K) {                    // the second block of a half pair: weight 0
+                        memset(out + 8 * q, 0x88, 8);
+                        continue;
+                    }
                     for (int i = 0; i < 4; ++i) {
                         out[8 * q + i] = (uint8_t)((wr[k0 + i] + 8) | ((wr[k0 + 4 + i] + 8) << 4));
                         out[8 * q + 4 + i] = (uint8_t)((wr[k0 + 8 + i] + 8) | ((wr[k0 + 12 + i] + 8) << 4));

@@ -228,10 +228,10 @@ bool dims_ok(const moe_prefill_params_t& p, std::string* why)
         *why = m;
         return false;
     };
-    if (p.d_model < 64 || p.d_model > 16384 || p.d_model % 64) return bad("d_model must be a multiple of 64 in [64, 16384]");
-    if (p.d_ff < 64 || p.d_ff > 16384 || p.d_ff % 64) return bad("d_ff must be a multiple of 64 in [64, 16384]");
+    if (p.d_model < 32 || p.d_model > 16384 || p.d_model % 32) return bad("d_model must be a multiple of 32 in [32, 16384]");
+    if (p.d_ff < 32 || p.d_ff > 16384 || p.d_ff % 32) return bad("d_ff must be a multiple of 32 in [32, 16384]");
     if (p.n_experts < 1 || p.n_experts > 1024) return bad("n_experts must be in [1, 1024]");
-    if (p.top_k < 1 || p.top_k > p.n_experts || p.top_k > 64) return bad("top_k must be in [1, min(n_experts, 64)]");
+    if (p.top_k < 1 || p.top_k > p.n_experts) return bad("top_k must be in [1, n_experts]");
     if (p.max_tokens < 1 || (int64_t)p.max_tokens * p.top_k > (1 << 21)) return bad("max_tokens must be >= 1 and max_tokens*top_k <= 2^21");
     return true;
 }
@@ -585,7 +585,7 @@ const char* moe_prefill_last_error(const moe_prefill_t* h)
 
 uint64_t moe_prefill_expert_bytes(int32_t d_model, int32_t d_ff)
 {
-    if (d_model < 64 || d_model % 64 || d_ff < 64 || d_ff % 64) return 0;
+    if (d_model < 32 || d_model % 32 || d_ff < 32 || d_ff % 32 || d_model > 16384 || d_ff > 16384) return 0;
     return blob_layout(d_model, d_ff).expert_bytes;
 }
 
@@ -598,8 +598,8 @@ uint64_t moe_prefill_layer_bytes(int32_t d_model, int32_t d_ff, int32_t n_expert
 int moe_prefill_pack_expert(int32_t d_model, int32_t d_ff, const int8_t* wgu_q, const uint16_t* wgu_s,
                             const int8_t* wd_q, const uint16_t* wd_s, void* dst)
 {
-    if (d_model < 64 || d_model % 64 || d_ff < 64 || d_ff % 64 || d_model > 16384 || d_ff > 16384)
-        return fail(nullptr, MOE_EINVAL, "pack: d_model and d_ff must be multiples of 64 in [64, 16384]");
+    if (d_model < 32 || d_model % 32 || d_ff < 32 || d_ff % 32 || d_model > 16384 || d_ff > 16384)
+        return fail(nullptr, MOE_EINVAL, "pack: d_model and d_ff must be multiples of 32 in [32, 16384]");
     if (!wgu_q || !wgu_s || !wd_q || !wd_s || !dst) return fail(nullptr, MOE_EINVAL, "pack: null pointer");
     if (!pack_expert(d_model, d_ff, wgu_q, wgu_s, wd_q, wd_s, static_cast<uint8_t*>(dst)))
         return fail(nullptr, MOE_EINVAL, "pack: weight outside [-8, 7]");

@@ -23,6 +23,7 @@ BLOCK_TESTS = {
     "valu_sub": 7,
     "overlap_indep": 8,    # two int8 MFMAs beside 64 fmas that do not depend on them
     "pipe_cvt_fma": 9,     # cvt_fma_mscale with the epilogue one block behind the MFMAs
+    "mfma_f32_scale": 10,  # the fp32 scale-product MFMA (v_mfma_f32_32x32x1_2b_f32) alone
 }
 
 

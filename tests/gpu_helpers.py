@@ -113,12 +113,19 @@ def assert_equal(name, a, ref):
                              f"got {a[i]!r} ref {ref[i]!r}")
 
 
+def weights_rtol(k: int) -> float:
+    """Router weights: fp32 (exp, an ascending sum of k terms, one division) against the
+    fp64 oracle.  2e-6 up to k = 8; beyond, the sum's rounding bound (k - 1) * 2^-24 of
+    the total grows with k, so the bound grows by 2^-23 per slot."""
+    return 2e-6 + max(0, k - 8) * 2.0 ** -23
+
+
 def check_full_parity(w: wl.Workload, g: dict, ref: dict):
     """Every stage of one layer: integers bit-exact, GU/H (which decide Hq) bit-exact,
     fp outputs within 1e-3 relative + 1e-4 absolute of the fp64 oracle."""
     T = ref["eidx"].shape[0]
     assert_equal("eidx", g["eidx"], ref["eidx"])
-    assert_close("weights", g["weights"], ref["w"], rtol=2e-6, atol=1e-7)
+    assert_close("weights", g["weights"], ref["w"], rtol=weights_rtol(w.k), atol=1e-7)
     assert_equal("counts", g["counts"], ref["counts"])
     assert_equal("bounds", g["bounds"], ref["bounds"])
     assert_equal("rows", g["rows"], ref["rows"])

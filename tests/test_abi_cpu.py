@@ -72,10 +72,14 @@ def test_errors_reach_stderr_when_MOE_LOG_LEVEL_is_set(capfd, monkeypatch):
 
 def test_dimension_checks():
     for bad in [(100, 512, 8, 2, 64), (256, 500, 8, 2, 64), (256, 512, 0, 1, 64), (256, 512, 8, 9, 64),
-                (256, 512, 8, 2, 0), (256, 512, 2000, 2, 64), (256, 512, 128, 65, 64)]:
+                (256, 512, 8, 2, 0), (256, 512, 2000, 2, 64), (256, 512, 128, 129, 64), (16, 512, 8, 2, 64),
+                (256, 16400, 8, 2, 64), (256, 512, 1024, 1024, 4096)]:
         with pytest.raises(mp.MoePrefillError) as ei:
             mp.moe_prefill_workspace_size(*bad)
         assert ei.value.code == mp.MOE_EINVAL
+    # multiples of 32 (one Q8/Q4 block) and any top_k up to n_experts are accepted
+    for ok in [(224, 96, 8, 2, 64), (32, 32, 1, 1, 1), (256, 512, 128, 65, 64), (64, 64, 1024, 1024, 2048)]:
+        assert mp.moe_prefill_workspace_size(*ok) > 0
     a = mp.moe_prefill_workspace_size(2048, 768, 128, 8, 1024)
     b = mp.moe_prefill_workspace_size(2048, 768, 128, 8, 2048)
     assert 0 < a < b
@@ -88,6 +92,10 @@ def test_blob_sizes():
     assert mp.moe_prefill_layer_bytes(2048, 768, 128) == 128 * eb
     assert mp.moe_prefill_layer_bytes(2048, 768, 128) == 324 * MiB
     assert mp.moe_prefill_expert_bytes(100, 768) == 0
+    # K % 64 == 32: the last K pair of every n-tile is stored whole (one block of zero codes)
+    pad = lambda x: (x + 255) // 256 * 256
+    assert mp.moe_prefill_expert_bytes(224, 96) == (pad(2 * 96 * 4 * 32) + pad(2 * 96 * 8 * 2) +
+                                                    pad(224 * 2 * 32) + pad(224 * 8 * 2))
 
 
 # ------------------------------------------------------------- planner ---
@@ -251,10 +259,11 @@ def test_oversized_struct_with_nonzero_tail_is_rejected():
 # -------------------------------------------------------------- packer ---
 
 def _unpack_blob_matrix(buf: np.ndarray, N: int, K: int, interleave_f: int):
-    """Read the tiled Q4 layout back, following the header's documented format."""
+    """Read the tiled Q4 layout back, following the header's documented format (with
+    K % 64 == 32 the padded second block of the last pair must hold code 8, weight 0)."""
     sx4 = lambda v: v - 8                        # offset-binary nibble
-    npairs, nbk = K // 64, K // 32
-    qs = buf[: N * K // 2].reshape(N // 32, npairs, 64, 16)
+    npairs, nbk = -(-K // 64), K // 32
+    qs = buf[: N * npairs * 32].reshape(N // 32, npairs, 64, 16)
     W = np.zeros((N, K), np.int8)
     for nt in range(N // 32):
         for lane in range(64):
@@ -264,6 +273,9 @@ def _unpack_blob_matrix(buf: np.ndarray, N: int, K: int, interleave_f: int):
                 by = [int(v) for v in qs[nt, pr, lane]]
                 for q in range(2):
                     k0 = 32 * (2 * pr + q) + 16 * h
+                    if k0 >= K:
+                        assert by[8 * q: 8 * q + 8] == [0x88] * 8
+                        continue
                     for i in range(4):
                         W[n, k0 + i] = sx4(by[8 * q + i] & 15)
                         W[n, k0 + 4 + i] = sx4(by[8 * q + i] >> 4)
@@ -272,7 +284,7 @@ def _unpack_blob_matrix(buf: np.ndarray, N: int, K: int, interleave_f: int):
     return W
 
 
-@pytest.mark.parametrize("d,f", [(128, 64), (320, 192)])
+@pytest.mark.parametrize("d,f", [(128, 64), (320, 192), (224, 96), (32, 32)])
 def test_pack_expert_layout_round_trip(d, f):
     r = np.random.default_rng(0)
     wgu_q = r.integers(-8, 8, (2 * f, d)).astype(np.int8)
@@ -283,10 +295,11 @@ def test_pack_expert_layout_round_trip(d, f):
     out = np.zeros(eb, np.uint8)
     mp.moe_prefill_pack_expert(d, f, wgu_q, wgu_s, wd_q, wd_s, out.ctypes.data)
     ngd, ngf = -(-(d // 32) // 8), -(-(f // 32) // 8)     # 8-block scale groups
-    gu_q_bytes = 2 * f * d // 2
-    gu_s_off = gu_q_bytes
+    pairs = lambda K: -(-K // 64)
+    gu_q_bytes = 2 * f * pairs(d) * 32
+    gu_s_off = (gu_q_bytes + 255) // 256 * 256
     d_q_off = gu_s_off + ((2 * f * ngd * 8 * 2 + 255) // 256) * 256
-    d_s_off = d_q_off + ((d * f // 2 + 255) // 256) * 256
+    d_s_off = d_q_off + ((d * pairs(f) * 32 + 255) // 256) * 256
     assert eb == d_s_off + ((d * ngf * 8 * 2 + 255) // 256) * 256
     assert np.array_equal(_unpack_blob_matrix(out, 2 * f, d, f), wgu_q)
     assert np.array_equal(_unpack_blob_matrix(out[d_q_off:], d, f, 0), wd_q)

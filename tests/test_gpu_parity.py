@@ -52,6 +52,11 @@ def test_resident_real_shape_all_stages():
     (129, 192, 320, 5, 5, None),        # k = E: every expert gets every token
     (70, 64, 64, 257, 8, None),         # E > 256: 16 routing keys per lane
     (40, 64, 64, 1024, 12, None),       # the largest E
+    (50, 224, 96, 6, 3, None),          # d and f odd multiples of 32: one-block K tail, one f-block group
+    (33, 32, 32, 4, 2, None),           # the smallest d and f: a single K block
+    (24, 64, 64, 100, 80, None),        # top_k above 64, rank-count routing (E <= 128)
+    (40, 96, 160, 300, 100, None),      # top_k above 64, wave-maximum routing (E > 128)
+    (8, 32, 64, 1024, 1024, None),      # k = E = 1024: every token goes to every expert
 ])
 def test_edge_shapes(T, d, f, E, k, bias):
     w = wl.small_workload(T, d, f, E, k, seed_base=77 + T + E, bias=bias)
@@ -63,10 +68,12 @@ def test_edge_shapes(T, d, f, E, k, bias):
 
 def test_tile_row_counts_at_every_group_boundary():
     """Experts with row counts on both sides of every 8-row register group of a
-    GEMM row tile (1 .. 97 rows: one and two 32-row halves, partly filled halves of
-    1-4 groups, full tiles plus a tail): k = 1 and each token's logit for its
-    assigned expert raised by 12, so the counts are exact."""
-    counts = [1, 7, 8, 9, 16, 17, 24, 25, 31, 32, 33, 40, 41, 48, 49, 56, 57, 63, 64, 65, 72, 97]
+    GEMM row tile (128 rows = two 64-row halves, each one or two 32-row register
+    halves): 1 .. 300 rows, i.e. partly filled groups in either half, an empty or
+    partly filled second half, full tiles plus a tail of every kind; k = 1 and each
+    token's logit for its assigned expert raised by 12, so the counts are exact."""
+    counts = [1, 7, 8, 9, 16, 17, 24, 25, 31, 32, 33, 40, 41, 48, 49, 56, 57, 63, 64, 65, 72, 97,
+              104, 120, 127, 128, 129, 160, 192, 193, 255, 256, 257, 300]
     E, k, d, f = len(counts) + 2, 1, 128, 192         # two experts get no rows
     T = sum(counts)
     w = wl.small_workload(T, d, f, E, k, seed_base=4242)
