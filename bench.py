@@ -327,10 +327,13 @@ def down_bytes(w, active: int) -> int:
     return wd + R * w.f + R * (w.f // 32) * 4 + R * w.d * 4
 
 
-def resident_leg(mp, wl, torch, dev, key: str, steps: int, warmup: int, micro, graph: bool = False) -> dict:
+def resident_leg(mp, wl, torch, dev, key: str, steps: int, warmup: int, micro, graph: bool = False,
+                 events_in_timed: bool = True) -> dict:
     """One resident layer of workload `key`, layer 0: W untimed layers, then K timed layers
     with HIP events between the kernels on the launch stream (the per-kernel device times of
-    exactly the timed region), the gate/up GEMM's roofline and the memory-bound kernels' GB/s."""
+    exactly the timed region), the gate/up GEMM's roofline and the memory-bound kernels' GB/s.
+    events_in_timed=False: the K timed layers run without events and K more give the kernel
+    times (a short layer's time is then free of the events' own cost)."""
     w = wl.WORKLOADS[key]
     T, d, f, E, k = w.T, w.d, w.f, w.E, w.k
     R = T * k
@@ -354,6 +357,13 @@ def resident_leg(mp, wl, torch, dev, key: str, steps: int, warmup: int, micro, g
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    us_plain = None
+    if not events_in_timed:       # the layer time without events, then the kernel times with them
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        us_plain = (time.perf_counter() - t0) * 1e6 / steps
     mp.moe_prefill_set_timing(h, True)
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -362,7 +372,7 @@ def resident_leg(mp, wl, torch, dev, key: str, steps: int, warmup: int, micro, g
     t1 = time.perf_counter()
     kt = mp.moe_prefill_kernel_times(h, reset=True)
     mp.moe_prefill_set_timing(h, False)
-    us = (t1 - t0) * 1e6 / steps
+    us = (t1 - t0) * 1e6 / steps if us_plain is None else us_plain
     kern_us = {n: (ms / c * 1e3 if c else None) for n, (c, ms) in kt.items()}
     gu_us, dn_us = kern_us["gemm_gate_up"], kern_us["gemm_down"]
     ops_gu = 2.0 * R * (2 * f) * d           # int8 multiply-adds x 2, routed rows only
@@ -445,7 +455,7 @@ def graph_leg(mp, torch, h, x, lg, y, blob, stream, steps, warmup, T) -> dict:
 def cpu_leg(wl, w, seconds: float) -> dict:
     """The CPU oracle as it stands, on the host's cores, on a bounded sample of the layer:
     routing, grouping and Q8 of all T tokens plus every stage of the sampled tokens' rows.
-    A 64-token probe sizes the sample to about `seconds` of oracle time."""
+    Two probes (64 and 256 tokens) size the sample to about `seconds` of oracle time."""
     import numpy as np
 
     import oracle
@@ -467,9 +477,11 @@ def cpu_leg(wl, w, seconds: float) -> dict:
         oracle.layer(x, lg, w.k, cache.__getitem__, w.f, tokens=toks)
         return time.perf_counter() - t0
 
-    probe = perm[:64]
-    tp = timed(probe)
-    n = int(min(w.T, max(64, round(64 * seconds / max(tp, 1e-3)))))
+    t64 = timed(perm[:64])                  # two probes: fixed cost (all tokens' routing, grouping,
+    t256 = timed(perm[:256])                # Q8) + a cost per sampled token
+    per_tok = max((t256 - t64) / 192, 1e-6)
+    fixed = max(t64 - 64 * per_tok, 0.0)
+    n = int(min(w.T, max(256, round((seconds - fixed) / per_tok))))
     toks = perm[:n]
     t = timed(toks)
     return {"value": round(n / t, 1), "unit": "tokens/s per layer", "cores": oracle.num_threads(),
@@ -553,6 +565,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline's token sample")
     ap.add_argument("--no-micro", action="store_true", help="skip the microbenchmark denominators")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the headline layer (no denominators, no T=1024 layer, no streaming, no CPU "
+                         "baseline): the command the kernel-trace and counter profiles run")
     ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--no-active", action="store_true", help="skip the active-expert streaming comparison")
     ap.add_argument("--no-cpu", action="store_true")
@@ -600,6 +615,8 @@ def main() -> int:
         print(json.dumps({"stacks": out}), flush=True)
         return 0
     # ---- measured denominators first (this also brings the clocks to their loaded state)
+    if args.headline_only:
+        args.no_micro = args.no_stream = args.no_cpu = True
     micro = None
     if not args.no_micro:
         micro = micro_leg(torch, dev)
@@ -615,9 +632,13 @@ def main() -> int:
         f"{head['roofline']['achieved']} TOPS = {100 * head['roofline']['frac']:.2f}% of int8 peak")
 
     # ---- the real-shape resident layer (T=1024, d_model=2048, d_ff=768, E=128, top-8): HBM-bound GEMMs
-    c1 = resident_leg(mp, wl, torch, dev, "resident", args.steps, args.warmup, micro, graph=True)
-    log(f"[bench] {c1['workload']}: {c1['us_per_layer']:.1f} us/layer; gate/up GEMM "
-        f"{c1['roofline']['achieved']} GB/s = {100 * c1['roofline']['frac']:.1f}% of HBM")
+    c1 = None
+    if not args.headline_only:
+        # a short layer: its own warm-up to steady clocks and a longer timed run (extra key)
+        c1 = resident_leg(mp, wl, torch, dev, "resident", max(args.steps, 200), max(args.warmup, 300), micro,
+                          graph=True, events_in_timed=False)
+        log(f"[bench] {c1['workload']}: {c1['us_per_layer']:.1f} us/layer; gate/up GEMM "
+            f"{c1['roofline']['achieved']} GB/s = {100 * c1['roofline']['frac']:.1f}% of HBM")
 
     line = {
         "metric": "MoE prefill tokens/s per layer (1 GPU); int8 MFMA %peak; H2D GB/s hidden %",

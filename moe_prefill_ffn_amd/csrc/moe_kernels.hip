@@ -664,9 +664,16 @@ struct GemmItem {
 };
 
 // XCD x (dispatch is round-robin over the 8 XCDs) takes a contiguous range of row
-// tiles, all their n-groups, the tiles of more than 32 rows first.
+// tiles, all their n-groups, the tiles of more than 32 rows first.  Inside the range
+// the workgroups go by super-groups of kSuperNG n-groups: all the range's tiles of
+// n-groups 0-7, then of 8-15, ...  The workgroups an XCD runs at once then share
+// each weight slice among many tiles and each tile's activation rows among 8
+// n-groups, which keeps more of both in that XCD's L2 than taking each tile's n-groups
+// together (tile-major) or each n-group's tiles together (n-group-major).
 // False: this workgroup has no item.  Runs before the kernel picks its arithmetic
 // path, so the tile-list reads stay scalar loads.
+constexpr int kSuperNG = 8;
+
 __device__ __forceinline__ bool gemm_item(const GemmArgs& g, GemmItem& it)
 {
     const int NG = ((g.N >> 5) + 3) >> 2;                 // n-groups of 4 n-tiles
@@ -678,9 +685,18 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs& g, GemmItem& it)
         const int ta = xcd * tq + (xcd < tr ? xcd : tr);
         const int tn = tq + (xcd < tr ? 1 : 0);
         if (slot >= tn * NG) return false;                // uniform across the workgroup
-        const int k = slot / NG;                          // heavy tiles first in each range
-        ng = slot - k * NG;
-        const int o = g.order[ta + k];
+        const int full = NG / kSuperNG, per = tn * kSuperNG, sg = slot / per;
+        int k;
+        if (sg < full) {                                  // a whole super-group
+            const int rem = slot - sg * per;
+            k = rem / kSuperNG;
+            ng = sg * kSuperNG + rem % kSuperNG;
+        } else {                                          // the last, partial one
+            const int rem = slot - full * per, part = NG - full * kSuperNG;
+            k = rem / part;
+            ng = full * kSuperNG + rem % part;
+        }
+        const int o = g.order[ta + k];                    // heavy tiles first in each range
         tile = o < 0 ? 0 : (o >= nt_all ? nt_all - 1 : o);   // a no-op for a sound order
     }
     const int te = g.tiles[3 * tile + 0];
