@@ -568,6 +568,8 @@ def main() -> int:
     ap.add_argument("--headline-only", action="store_true",
                     help="only the headline layer (no denominators, no T=1024 layer, no streaming, no CPU "
                          "baseline): the command the kernel-trace and counter profiles run")
+    ap.add_argument("--workload", default="skew", choices=("skew", "resident"),
+                    help="with --headline-only: the layer to run (the T=1024 layer for its own profiles)")
     ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--no-active", action="store_true", help="skip the active-expert streaming comparison")
     ap.add_argument("--no-cpu", action="store_true")
@@ -615,6 +617,9 @@ def main() -> int:
         print(json.dumps({"stacks": out}), flush=True)
         return 0
     # ---- measured denominators first (this also brings the clocks to their loaded state)
+    if args.workload != "skew" and not args.headline_only:
+        print("--workload applies to --headline-only runs", file=sys.stderr)
+        return 2
     if args.headline_only:
         args.no_micro = args.no_stream = args.no_cpu = True
     micro = None
@@ -625,8 +630,8 @@ def main() -> int:
 
     # ---- headline: the largest single-GPU configuration, one resident layer of the skewed
     # 8-layer stack's shape (T=8192, d_model=4096, d_ff=1536, E=256, top-8, Zipf routing)
-    head = resident_leg(mp, wl, torch, dev, "skew", args.steps, args.warmup, micro)
-    w = wl.WORKLOADS["skew"]
+    head = resident_leg(mp, wl, torch, dev, args.workload, args.steps, args.warmup, micro)
+    w = wl.WORKLOADS[args.workload]
     log(f"[bench] headline {w.name}: {head['us_per_layer']:.1f} us/layer -> "
         f"{head['tokens_per_s_per_layer']:,.0f} tokens/s per layer; gate/up GEMM "
         f"{head['roofline']['achieved']} TOPS = {100 * head['roofline']['frac']:.2f}% of int8 peak")
