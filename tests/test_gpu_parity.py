@@ -87,6 +87,37 @@ def test_tile_row_counts_at_every_group_boundary():
     check_full_parity(w, g, ref)
 
 
+def test_gemm_block_combination_worked_example():
+    """The hand-derived case of tests/golden/gemm_block_order_worked_example.json run
+    through the kernels: x is chosen so that its Q8 codes and scales are the example's
+    (block 0: code -1 at k = 0, scale 1; block 1: code 3 at k = 32, scale 0x3EAAAAAB),
+    and gate row 0 of the single expert holds weight 1 at k = 0 and k = 32 with fp16
+    scales 1.0.  GU[0, 0] must be 2^-25 (one fma per block, ascending), the value
+    neither a separate multiply nor the other block order gives."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "gemm_block_order_worked_example.json")))
+    T, d, f, E, k = 1, 64, 32, 1, 1
+    w = wl.small_workload(T, d, f, E, k, seed_base=9)
+    x = np.zeros((T, d), np.float32)
+    x[0, 0], x[0, 1] = -1.0, 127.0               # block 0: amax 127 -> scale 1, codes -1, 127
+    x[0, 32], x[0, 33] = 1.0, 42.333336          # block 1: scale 0x3EAAAAAB, code 3 at k = 32
+    lg = np.zeros((T, E), np.float32)
+    base = wl.expert_weights(w, 0, 0)
+    wgu_q = base.wgu_q.copy()
+    wgu_s = base.wgu_s.copy()
+    wgu_q[0, :] = 0
+    wgu_q[0, 0] = wgu_q[0, 32] = 1
+    wgu_s[0, :] = 0x3C00
+    ex = wl.ExpertWeights(wgu_q, wgu_s, base.wd_q, base.wd_s)
+    g_, ref = _full_case(w, x=x, lg=lg, override=lambda e: ex)
+    assert ref["xq"][0, 0] == -1 and ref["xq"][0, 32] == 3
+    assert ref["dx"].view(np.uint32)[0, 1] == int(g["a_scales_bits"][1], 16)
+    assert ref["gu"].view(np.uint32)[0, 0] == int(g["expected_bits"], 16)
+    assert g_["gu"].view(np.uint32)[0, 0] == int(g["expected_bits"], 16)
+    check_full_parity(w, g_, ref)
+
+
 @pytest.mark.parametrize("name", ["tiny", "resident"])
 def test_hot_path_without_intermediate_exports(name):
     """The bench configuration: GU and H are not exported, so the gate/up GEMM

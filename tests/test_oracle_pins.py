@@ -283,3 +283,23 @@ def test_combine_matches_einsum(oracle_lib):
     onehot = np.zeros((T, k))
     onehot[:, 1] = 1.0
     assert np.array_equal(oracle.combine_f64(onehot, pos, dm), dm[pos[:, 1]])
+
+
+def test_gemm_block_combination_worked_example():
+    """R9 pinned by a hand-derived case (tests/golden/gemm_block_order_worked_example.json):
+    one fused multiply-add per block in ascending block order gives 2^-25; a separate
+    multiply and add, or the reverse block order, gives 0.0."""
+    g = json.load(open(os.path.join(GOLDEN, "gemm_block_order_worked_example.json")))
+    K = g["K"]
+    A = np.zeros((1, K), np.int8)
+    W = np.zeros((1, K), np.int8)
+    for k, v in g["a_codes"].items():
+        A[0, int(k)] = v
+    for k, v in g["w_codes"].items():
+        W[0, int(k)] = v
+    a_scale = np.array([[int(b, 16) for b in g["a_scales_bits"]]], np.uint32).view(np.float32)
+    w_scale = np.array([[int(b, 16) for b in g["w_scales_fp16_bits"]]], np.uint16)
+    out = oracle.gemm_f32(A, a_scale, W, w_scale)
+    assert out.view(np.uint32)[0, 0] == int(g["expected_bits"], 16)
+    assert out[0, 0] == np.float32(2.0 ** -25)
+    assert int(g["mul_then_add_bits"], 16) != int(g["expected_bits"], 16)
