@@ -417,6 +417,23 @@ def resident_leg(mp, wl, torch, dev, key: str, steps: int, warmup: int, micro, g
                 "combine_GBs": round(c_bytes / (kern_us["combine"] * 1e-6) / 1e9, 1),
                 "route_quant_bytes": q_bytes, "combine_bytes": c_bytes, "peak_GBs": HBM_PEAK_GBS},
     }
+    # the whole layer against its floor: its int8 ops at the spec peak (and at the measured
+    # per-block epilogue ceiling), or its unavoidable HBM bytes (the active experts' weights,
+    # x, logits, y) at 8 TB/s, whichever is longer
+    ops_layer = ops_gu + ops_dn
+    min_bytes = active * mp.moe_prefill_expert_bytes(d, f) + T * d * 4 * 2 + T * E * 4
+    floor_ops_us = ops_layer / (INT8_PEAK_TOPS * 1e12) * 1e6
+    floor_hbm_us = min_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
+    floor_us = max(floor_ops_us, floor_hbm_us)
+    out["layer_roofline"] = {
+        "bound": "mfma" if floor_ops_us >= floor_hbm_us else "hbm", "floor_us": round(floor_us, 2),
+        "frac": round(floor_us / us, 4), "int8_ops_per_layer": ops_layer, "min_hbm_bytes_per_layer": min_bytes,
+        "floor_us_at_int8_peak": round(floor_ops_us, 2), "floor_us_at_hbm_peak": round(floor_hbm_us, 2),
+    }
+    if micro:
+        ceil_us = ops_layer / (micro["epilogue_ceiling_TOPS"] * 1e12) * 1e6
+        out["layer_roofline"]["floor_us_at_epilogue_ceiling"] = round(ceil_us, 2)
+        out["layer_roofline"]["frac_of_epilogue_ceiling_floor"] = round(max(ceil_us, floor_hbm_us) / us, 4)
     if graph:
         out["graph_replay"] = graph_leg(mp, torch, h, x, lg, y, blob, stream, steps, warmup, T)
     h.close()
@@ -654,7 +671,8 @@ def main() -> int:
                 "Q4 uniform int4 weights)",
         "config": {"workload": w.name, "T": w.T, "d_model": w.d, "d_ff": w.f, "n_experts": w.E, "top_k": w.k,
                    "weights": "resident in HBM", "global_batch": w.T, "seq_len": w.T, "parallelism": "none"},
-        "roofline": head["roofline"], "kernels_us": head["kernels_us"], "hbm": head["hbm"],
+        "roofline": head["roofline"], "layer_roofline": head["layer_roofline"],
+        "kernels_us": head["kernels_us"], "hbm": head["hbm"],
         "gemm_down": head["gemm_down"], "denominators": micro,
         "resident_c1": c1,
     }

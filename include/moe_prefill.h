@@ -92,15 +92,23 @@ int moe_prefill_workspace_size(const moe_prefill_params_t* p, uint64_t* bytes);
 
 /* Checks the dimensions and the device (gfx950, else MOE_EUNSUPPORTED),
  * allocates or adopts the workspace, creates the copy stream and events.
- * On failure *out is NULL. */
+ * The handle holds every buffer one layer of the prompt path needs (page #663,
+ * "What": the stages' prompt buffers, the row table and the group bounds); the
+ * workspace is the one mandatory resource, so a failed allocation is MOE_ENOMEM
+ * with no fallback (page #1906, pool-behaviour table: mandatory execution
+ * memory fails clearly).  On failure *out is NULL. */
 int moe_prefill_create(const moe_prefill_params_t* p, moe_prefill_t** out);
 
-/* Waits for the handle's copy stream, releases the pool, events, streams and
- * a library-owned workspace.  NULL is a no-op. */
+/* Waits for the handle's copy stream, then releases the pool, events, streams
+ * and a library-owned workspace, so no queued copy writes into freed memory
+ * (page #1906, "Verification": lifecycle cleanup of the pool is among the
+ * validated behaviours).  NULL is a no-op. */
 void moe_prefill_destroy(moe_prefill_t* h);
 
 /* Message of the last failure on h (h may be NULL: the last failure of a call
- * that had no handle, per thread).  Never NULL; "" after success. */
+ * that had no handle, per thread).  Never NULL; "" after success.  Failures are
+ * reported clearly rather than hidden behind a fallback (page #1906,
+ * pool-behaviour table). */
 const char* moe_prefill_last_error(const moe_prefill_t* h);
 
 /* ---------------------------------------------------------- weight blob --- */
@@ -222,8 +230,12 @@ typedef struct stream_pool_params {
     int64_t reserve_bytes;           /* > 0: device memory to keep free.  When a pass starts
                                         (moe_prefill_run_layer with layer 0) and the device
                                         has less free memory than this, the pool shrinks by
-                                        the difference as stream_pool_set_budget does.
-                                        0: off */
+                                        the difference as stream_pool_set_budget does: that
+                                        layer-0 call then waits on the host (bounded) for the
+                                        released slots' queued work, so it must not be
+                                        captured in a HIP graph; callers that capture passes
+                                        leave this 0 and call stream_pool_set_budget between
+                                        passes.  0: off */
 } stream_pool_params_t;
 
 #define MOE_WARN_SLOT_OVER_BUDGET 1  /* the one mandatory slot exceeds max_vram_bytes */
@@ -349,7 +361,10 @@ typedef struct moe_stats {
     uint64_t pressure_trims;         /* shrinks started by reserve_bytes at a pass start */
 } moe_stats_t;
 
-/* Counters of the handle.  experts_loaded and bytes_sparse are kept on the
+/* Counters of the handle: layers run, prefetches queued against prefetches that
+ * a layer found ready (page #1905, "Verification": prefetches activated out of
+ * those queued), synchronous loads, bytes copied, and the pool's evictions.
+ * experts_loaded and bytes_sparse are kept on the
  * device; reading them waits for the device to finish its queued work. */
 int moe_prefill_get_stats(const moe_prefill_t* h, moe_stats_t* inout);
 
