@@ -96,3 +96,50 @@ def test_noalloc_equals_run_layer_on_consecutive_calls():
             assert_close("y vs oracle", y.cpu().numpy(), oracle.layer(x, lg, w.k, ex_tiny, w.f)["y"])
     h_big.close()
     h_tiny.close()
+
+
+@pytest.mark.gpu
+def test_noalloc_layer_captured_in_a_hip_graph_replays_exactly():
+    """The callers this entry point is for include code under HIP graph capture: one
+    resident layer captured once, replayed with new inputs copied into the captured
+    buffers and eager work (the handle-based entry point) between the replays; every
+    replay equals the eager run bit for bit."""
+    from gpu_helpers import ExpertCache, host_blob, say
+
+    w = wl.WORKLOADS["resident"]
+    say("[case] noalloc layer under graph capture")
+    T = 512
+    blob = host_blob(w, ExpertCache(w, 0, keep=False)).cuda()
+    xs = [torch.from_numpy(np.ascontiguousarray(wl.layer_activations(w, l)[:T])).cuda() for l in (0, 1, 2)]
+    lgs = [torch.from_numpy(np.ascontiguousarray(wl.layer_logits(w, l)[:T])).cuda() for l in (0, 1, 2)]
+    h = mp.moe_prefill_create(w.d, w.f, w.E, w.k, T)
+    ref = []
+    for x, lg in zip(xs, lgs):
+        y = torch.empty(T, w.d, device="cuda")
+        mp.moe_prefill_run_layer(h, x, lg, y, weights=blob)
+        torch.cuda.synchronize()
+        ref.append(y.cpu())
+    x_s, lg_s = xs[0].clone(), lgs[0].clone()
+    y_s = torch.empty(T, w.d, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mp.moe_prefill_run_layer_noalloc(w.d, w.f, w.E, w.k, x_s, lg_s, y_s, blob, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="thread_local"):
+        mp.moe_prefill_run_layer_noalloc(w.d, w.f, w.E, w.k, x_s, lg_s, y_s, blob)
+    for rep in range(3):
+        for i in (1, 0, 2):
+            x_s.copy_(xs[i])
+            lg_s.copy_(lgs[i])
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y_s.cpu(), ref[i]), (rep, i)
+            y_e = torch.empty_like(y_s)
+            mp.moe_prefill_run_layer(h, xs[i], lgs[i], y_e, weights=blob)
+            torch.cuda.synchronize()
+            assert torch.equal(y_e.cpu(), ref[i]), (rep, i, "eager")
+    del g
+    h.close()
