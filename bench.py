@@ -519,6 +519,15 @@ def micro_leg(torch, dev) -> dict:
     spec_mac_clk = INT8_PEAK_TOPS * 1e12 / 2 / (n_cu * 4 * 2.4e9)   # MACs per clock per SIMD at the spec
     out = {"n_cu": n_cu, "spec_int8_mac_per_clk_per_simd": round(spec_mac_clk, 1)}
     micro.block("mfma_i8", 2000, n_cu)                                # warm the clocks
+
+    def simd_cycles(r, iters):
+        """SIMD cycles per loop iteration: the launch's event time at the shader clock the
+        waves read over their loops.  Every SIMD holds the same waves for the whole launch
+        (n_cu x wps workgroups of four waves), so this is each SIMD's time; a wave's own
+        cycle count is not, since the SIMD issues oldest-first and the waves that start
+        first finish first."""
+        return r["ms"] * 1e-3 * r["clock_ghz"] * 1e9 / iters
+
     forms = {}
     for name, iters in (("mfma_i8", 40000), ("cvt_fma_mscale", 20000), ("cvt_fma_vscale", 20000),
                         ("sub_fma_vscale", 20000), ("sub_fma_mscale", 20000), ("pipe_cvt_fma", 20000),
@@ -526,7 +535,7 @@ def micro_leg(torch, dev) -> dict:
         for wps in (4, 2):
             r = micro.block(name, iters, n_cu, wps)
             macs_iter = (4 if name == "mfma_i8" else 2) * 32768
-            mac_clk = wps * macs_iter * iters / r["cycles_per_wave"]
+            mac_clk = wps * macs_iter / simd_cycles(r, iters)
             forms[f"{name}@{wps}w"] = {
                 "TOPS": round(r["work"] / (r["ms"] * 1e-3) / 1e12, 1),
                 "frac_of_spec_peak": round(r["work"] / (r["ms"] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
@@ -544,12 +553,25 @@ def micro_leg(torch, dev) -> dict:
     for name in ("valu_fma", "valu_cvt", "valu_sub"):
         iters = 20000
         r = micro.block(name, iters, n_cu, 4)
-        valu[name] = round(r["cycles_per_wave"] / (4 * 64 * iters), 3)   # SIMD cycles per wave64 instruction
+        valu[name] = round(simd_cycles(r, iters) / (4 * 64), 3)   # SIMD cycles per wave64 instruction
     out["valu_cycles_per_wave_instr"] = valu
+    # co-execution: SIMD cycles per loop iteration of the single-kind loops (per wave and
+    # iteration: 64 fmas, 64 converts, four int8 MFMAs, two scale-product MFMAs) beside the
+    # loops that issue both kinds (two int8 MFMAs + 64 fmas, two int8 MFMAs + 64 converts,
+    # one scale-product MFMA + 64 fmas), none depending on the other
+    coexec = {}
+    for wps in (1, 4):
+        row = {}
+        for name in ("valu_fma", "valu_cvt", "mfma_i8", "mfma_f32_scale", "overlap_indep", "overlap_cvt",
+                     "overlap_scale_fma"):
+            r = micro.block(name, 20000, n_cu, wps)
+            row[name] = round(simd_cycles(r, 20000), 1)
+        coexec[f"{wps}w"] = row
+    out["coexec_simd_cycles_per_iter"] = coexec
     iters = 20000
     r = micro.block("mfma_f32_scale", iters, n_cu, 4)
     # SIMD cycles per scale-product MFMA (4 waves per SIMD, 2 per iteration) and products/s
-    out["mfma_f32_scale"] = {"cycles_per_instr": round(r["cycles_per_wave"] / (4 * 2 * iters), 2),
+    out["mfma_f32_scale"] = {"cycles_per_instr": round(simd_cycles(r, iters) / (4 * 2), 2),
                              "G_products_per_s": round(r["work"] / 2 / (r["ms"] * 1e-3) / 1e9, 1)}
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)

@@ -23,13 +23,20 @@
 //   overlap_indep    two int8 MFMAs and 64 fmas that do not depend on them: how much
 //                    of the VALU work the matrix cores can run beside
 //   mfma_f32_scale   v_mfma_f32_32x32x1_2b_f32 alone (the scale-product MFMA)
+//   overlap_cvt / overlap_mul / overlap_fma16   two int8 MFMAs beside 64 independent
+//                    converts, 64 multiplies, or only 16 fmas
+//   overlap_scale_fma  one scale-product MFMA beside 64 independent fmas
 //   pipe_cvt_fma     cvt_fma_mscale with the epilogue one block behind the MFMAs
 //                    (the MFMAs of block b+1 issue before the VALU work of block b)
 //
 // Each loop iteration is one 32-block of a 64-row x 32-column wave tile: two
 // int8 MFMAs (64 x 32 x 32 MACs) and the epilogue of its 2048 elements (32 per
 // lane).  Four workgroups of four waves per CU put four waves on every SIMD.
-// Cycle counts come from the shader clock (s_memtime) around each wave's loop.
+// Each wave reads the shader clock (s_memtime) and the 100 MHz real-time counter
+// around its loop; their ratio is the shader clock over the loop.  A wave's own
+// cycle count is not the SIMD's time per iteration when several waves share a
+// SIMD (it issues oldest-first, so the first waves finish early): the SIMD's time
+// is the launch's event time at that clock.
 //
 // copy: a float4 grid-stride device copy (HBM read + write).
 // atomic: fp32 atomic adds without return into rows scattered like the
@@ -117,6 +124,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
             tp = __builtin_amdgcn_mfma_f32_32x32x1f32(dxv, dw, fzero, 0, 0, 0);
             t2 = __builtin_amdgcn_mfma_f32_32x32x1f32(dw, dxv, fzero, 0, 0, 0);
             asm volatile("" : "+v"(tp), "+v"(t2));
+            continue;
+        }
+        if (kTest == 11 || kTest == 13) {   // MFMAs beside 64 independent converts / multiplies
+            m0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b, m0, 0, 0, 0);
+            m1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b, m1, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (kTest == 11) {
+                    asm volatile("v_cvt_f32_i32 %0, %1" : "=v"(acc0[i]) : "v"(m2[i]));
+                    asm volatile("v_cvt_f32_i32 %0, %1" : "=v"(acc1[i]) : "v"(m3[i]));
+                    asm volatile("v_cvt_f32_i32 %0, %1" : "=v"(dxr[i]) : "v"(m2[i]));
+                    asm volatile("v_cvt_f32_i32 %0, %1" : "=v"(dxr[16 + i]) : "v"(m3[i]));
+                } else {
+                    asm volatile("v_mul_f32 %0, %1, %2" : "=v"(acc0[i]) : "v"(dxr[i]), "v"(dw));
+                    asm volatile("v_mul_f32 %0, %1, %2" : "=v"(acc1[i]) : "v"(dxr[16 + i]), "v"(dw));
+                    asm volatile("v_mul_f32 %0, %1, %2" : "=v"(acc0[i]) : "v"(dxr[16 + i]), "v"(dxv));
+                    asm volatile("v_mul_f32 %0, %1, %2" : "=v"(acc1[i]) : "v"(dxr[i]), "v"(dxv));
+                }
+            }
+            continue;
+        }
+        if (kTest == 12) {           // MFMAs beside 16 independent fmas
+            m0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b, m0, 0, 0, 0);
+            m1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b, m1, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc0[i]) : "v"(dxr[i]), "v"(dw));
+                asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc1[i]) : "v"(dxr[16 + i]), "v"(dw));
+            }
+            continue;
+        }
+        if (kTest == 14) {           // the scale-product MFMA beside 64 independent fmas
+            touchf(dxv);
+            touchf(dw);
+            tp = __builtin_amdgcn_mfma_f32_32x32x1f32(dxv, dw, fzero, 0, 0, 0);
+            asm volatile("" : "+v"(tp));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc0[i]) : "v"(dxr[i]), "v"(dw));
+                asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc1[i]) : "v"(dxr[16 + i]), "v"(dw));
+                asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc0[i]) : "v"(dxr[16 + i]), "v"(dxv));
+                asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc1[i]) : "v"(dxr[i]), "v"(dxv));
+            }
             continue;
         }
         if (kTest == 8) {            // MFMAs beside independent VALU work
@@ -231,11 +281,12 @@ typedef struct moe_micro_result {
 } moe_micro_result_t;
 
 // test: 0 mfma_i8, 1 cvt_fma_mscale, 2 cvt_fma_vscale, 3 sub_fma_vscale, 4 sub_fma_mscale,
-// 5 valu_fma, 6 valu_cvt, 7 valu_sub, 8 overlap_indep, 9 pipe_cvt_fma, 10 mfma_f32_scale.  blocks_per_cu workgroups of 256 threads on each of
+// 5 valu_fma, 6 valu_cvt, 7 valu_sub, 8 overlap_indep, 9 pipe_cvt_fma, 10 mfma_f32_scale,
+// 11 overlap_cvt, 12 overlap_fma16, 13 overlap_mul, 14 overlap_scale_fma.  blocks_per_cu workgroups of 256 threads on each of
 // n_cu compute units.  Returns 0 or a negative HIP error.
 int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_per_cu, moe_micro_result_t* res)
 {
-    if (!res || iters < 1 || n_cu < 1 || blocks_per_cu < 1 || test < 0 || test > 10) return -1;
+    if (!res || iters < 1 || n_cu < 1 || blocks_per_cu < 1 || test < 0 || test > 14) return -1;
     MicroOut* d_out = nullptr;
     hipEvent_t e0, e1;
     if (hipMalloc(&d_out, sizeof(MicroOut)) != hipSuccess) return -2;
@@ -255,7 +306,11 @@ int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_pe
     case 7: hipLaunchKernelGGL(k_block<7>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     case 8: hipLaunchKernelGGL(k_block<8>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     case 9: hipLaunchKernelGGL(k_block<9>, grid, blk, 0, nullptr, iters, 3, d_out); break;
-    default: hipLaunchKernelGGL(k_block<10>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 10: hipLaunchKernelGGL(k_block<10>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 11: hipLaunchKernelGGL(k_block<11>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 12: hipLaunchKernelGGL(k_block<12>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 13: hipLaunchKernelGGL(k_block<13>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    default: hipLaunchKernelGGL(k_block<14>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     }
     (void)hipEventRecord(e1, nullptr);
     hipError_t e = hipEventSynchronize(e1);
@@ -276,7 +331,8 @@ int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_pe
     // products (2 x 2048 per iteration); the VALU-only tests count none
     const double macs = test == 0 ? 4.0 * 32768.0
                       : test == 10 ? 2.0 * 2048.0
-                      : ((test <= 4 || test == 8 || test == 9) ? 2.0 * 32768.0 : 0.0);
+                      : test == 14 ? 2048.0
+                      : ((test <= 4 || (test >= 8 && test != 10)) ? 2.0 * 32768.0 : 0.0);
     res->work = 2.0 * macs * (double)iters * waves;
     return 0;
 }

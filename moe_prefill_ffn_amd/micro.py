@@ -24,6 +24,10 @@ BLOCK_TESTS = {
     "overlap_indep": 8,    # two int8 MFMAs beside 64 fmas that do not depend on them
     "pipe_cvt_fma": 9,     # cvt_fma_mscale with the epilogue one block behind the MFMAs
     "mfma_f32_scale": 10,  # the fp32 scale-product MFMA (v_mfma_f32_32x32x1_2b_f32) alone
+    "overlap_cvt": 11,     # two int8 MFMAs beside 64 independent converts
+    "overlap_fma16": 12,   # two int8 MFMAs beside 16 independent fmas
+    "overlap_mul": 13,     # two int8 MFMAs beside 64 independent multiplies
+    "overlap_scale_fma": 14,  # one scale-product MFMA beside 64 independent fmas
 }
 
 
