@@ -59,6 +59,7 @@ def test_resident_real_shape_all_stages():
     (8, 32, 64, 1024, 1024, None),      # k = E = 1024: every token goes to every expert
     (24, 16384, 16384, 2, 1, None),     # the largest d and f: 256 K pairs, 1,024 gate/up n-tiles
     (17, 16352, 16352, 3, 2, None),     # the largest odd multiples of 32: one-block K tails at K = 16352
+    (65536, 32, 32, 64, 32, None),      # T * top_k = 2^21, the largest routed-row count
 ])
 def test_edge_shapes(T, d, f, E, k, bias):
     w = wl.small_workload(T, d, f, E, k, seed_base=77 + T + E, bias=bias)
