@@ -328,7 +328,7 @@ def down_bytes(w, active: int) -> int:
 
 
 def resident_leg(mp, wl, torch, dev, key: str, steps: int, warmup: int, micro, graph: bool = False,
-                 events_in_timed: bool = True) -> dict:
+                 events_in_timed: bool = True, atomic: bool = False) -> dict:
     """One resident layer of workload `key`, layer 0: W untimed layers, then K timed layers
     with HIP events between the kernels on the launch stream (the per-kernel device times of
     exactly the timed region), the gate/up GEMM's roofline and the memory-bound kernels' GB/s.
@@ -436,10 +436,52 @@ def resident_leg(mp, wl, torch, dev, key: str, steps: int, warmup: int, micro, g
         out["layer_roofline"]["frac_of_epilogue_ceiling_floor"] = round(max(ceil_us, floor_hbm_us) / us, 4)
     if graph:
         out["graph_replay"] = graph_leg(mp, torch, h, x, lg, y, blob, stream, steps, warmup, T)
+    if atomic:
+        out["combine_atomic"] = atomic_leg(mp, torch, h, x, lg, y, blob, stream, steps, warmup, T, us,
+                                           events_in_timed)
     h.close()
     del blob, x, lg, y
     torch.cuda.empty_cache()
     return out
+
+
+def atomic_leg(mp, torch, h, x, lg, y, blob, stream, steps, warmup, T, us_gather,
+               events_in_timed: bool = True) -> dict:
+    """The same layer with the opt-in atomic combine (the down GEMM adds w * Dm into y,
+    no Dm round trip, no gather kernel): its time and kernel times, timed the way the
+    gather's layer time was, and its largest difference from the gather's y (the order
+    of the fp32 adds varies)."""
+    y_ref = y.clone()
+    y_at = torch.empty_like(y)
+
+    def step():
+        mp.moe_prefill_run_layer(h, x, lg, y_at, layer=-1, weights=blob, stream=stream, combine="atomic")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    us_plain = None
+    if not events_in_timed:
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        us_plain = (time.perf_counter() - t0) * 1e6 / steps
+    mp.moe_prefill_set_timing(h, True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    us_at = (time.perf_counter() - t0) * 1e6 / steps if us_plain is None else us_plain
+    kt = mp.moe_prefill_kernel_times(h, reset=True)
+    mp.moe_prefill_set_timing(h, False)
+    diff = (y_at - y_ref).abs().max().item()
+    scale = y_ref.abs().max().item()
+    return {"us_per_layer": round(us_at, 2), "tokens_per_s_per_layer": round(T / (us_at * 1e-6), 1),
+            "saving_us_vs_gather": round(us_gather - us_at, 2),
+            "kernels_us": {n: (round(ms / c * 1e3, 2) if c else None) for n, (c, ms) in kt.items()},
+            "max_abs_diff_vs_gather": diff, "max_abs_y": scale,
+            "note": "gemm_down includes zeroing y and the atomic adds; combine is only the mask clear"}
 
 
 def graph_leg(mp, torch, h, x, lg, y, blob, stream, steps, warmup, T) -> dict:
@@ -669,7 +711,10 @@ def main() -> int:
 
     # ---- headline: the largest single-GPU configuration, one resident layer of the skewed
     # 8-layer stack's shape (T=8192, d_model=4096, d_ff=1536, E=256, top-8, Zipf routing)
-    head = resident_leg(mp, wl, torch, dev, args.workload, args.steps, args.warmup, micro)
+    # (the opt-in atomic combine is timed as an extra key, outside --headline-only, whose
+    # kernel traces must hold the default path's launches only)
+    head = resident_leg(mp, wl, torch, dev, args.workload, args.steps, args.warmup, micro,
+                        atomic=not args.headline_only)
     w = wl.WORKLOADS[args.workload]
     log(f"[bench] headline {w.name}: {head['us_per_layer']:.1f} us/layer -> "
         f"{head['tokens_per_s_per_layer']:,.0f} tokens/s per layer; gate/up GEMM "
@@ -680,7 +725,7 @@ def main() -> int:
     if not args.headline_only:
         # a short layer: its own warm-up to steady clocks and a longer timed run (extra key)
         c1 = resident_leg(mp, wl, torch, dev, "resident", max(args.steps, 200), max(args.warmup, 300), micro,
-                          graph=True, events_in_timed=False)
+                          graph=True, events_in_timed=False, atomic=True)
         log(f"[bench] {c1['workload']}: {c1['us_per_layer']:.1f} us/layer; gate/up GEMM "
             f"{c1['roofline']['achieved']} GB/s = {100 * c1['roofline']['frac']:.1f}% of HBM")
 
@@ -695,7 +740,7 @@ def main() -> int:
                    "weights": "resident in HBM", "global_batch": w.T, "seq_len": w.T, "parallelism": "none"},
         "roofline": head["roofline"], "layer_roofline": head["layer_roofline"],
         "kernels_us": head["kernels_us"], "hbm": head["hbm"],
-        "gemm_down": head["gemm_down"], "denominators": micro,
+        "gemm_down": head["gemm_down"], "combine_atomic": head.get("combine_atomic"), "denominators": micro,
         "resident_c1": c1,
     }
     # ---- streamed stack: 4 layers through a 2-slot pool with depth-1 prefetch

@@ -163,7 +163,27 @@ typedef struct moe_layer_io {
     int8_t* hq;                /* [T*k, f]  Q8 codes of h */
     float* dh;                 /* [T*k, f/32] Q8 scales of h */
     float* dm;                 /* [T*k, d]  down projection per row */
+    /* Fields added after the first layout (a caller built against that layout
+       passes its smaller struct_size and gets the defaults): */
+    int32_t combine;           /* how the expert rows become token rows (the
+                                  combine step, page #663 "What"):
+                                  MOE_COMBINE_GATHER (0, default): the down GEMM
+                                  writes Dm and a gather kernel sums each token's
+                                  k rows in slot order -- deterministic, the
+                                  same bits on every run;
+                                  MOE_COMBINE_ATOMIC (1): the down GEMM's epilogue
+                                  adds w * Dm straight into y with fp32 atomic
+                                  adds (y is zeroed first), so Dm never goes
+                                  through device memory.  The order of the adds
+                                  changes from run to run, so y agrees with the
+                                  gather only to rounding (page #663 "Output":
+                                  another grouping rounds differently; such a
+                                  variant is opt-in).  dm cannot be exported in
+                                  this mode (MOE_EINVAL). */
+    int32_t reserved1;         /* 0 */
 } moe_layer_io_t;
+
+enum { MOE_COMBINE_GATHER = 0, MOE_COMBINE_ATOMIC = 1 };
 
 /*
  * Runs one MoE prefill FFN layer on `stream` (see the file comment for the
@@ -173,8 +193,9 @@ typedef struct moe_layer_io {
  * (load-then-compute, page #1905 "Summary").  After enqueueing the layer it
  * queues prefetches of the next prefetch-depth streamed layers on the copy
  * stream; a prefetch never overwrites the active slot.
- * Errors: MOE_EINVAL (bad T or pointers), MOE_ESTATE (layer >= 0 with no pool,
- * or layer out of range), MOE_EHIP.
+ * Errors: MOE_EINVAL (bad T or pointers, an unknown combine mode, dm with
+ * MOE_COMBINE_ATOMIC), MOE_ESTATE (layer >= 0 with no pool, or layer out of
+ * range), MOE_EHIP.
  */
 int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io, void* stream);
 
@@ -188,7 +209,8 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io, void* stre
  *    limits as moe_prefill_create; max_tokens is ignored (the workspace is laid
  *    out for io->n_tokens) and workspace must be NULL.
  *  - io: as for moe_prefill_run_layer, resident weights only (layer == -1,
- *    weights_dev set); the optional exports work as there.
+ *    weights_dev set); the optional exports and the combine modes work as
+ *    there.
  *  - The workspace is a static device array of 128 MiB (134217728 bytes) per
  *    device, 256-byte aligned, that the library holds until the process ends.
  *    A layer whose workspace (moe_prefill_workspace_size with max_tokens =

@@ -49,7 +49,10 @@ class moe_layer_io_t(ctypes.Structure):
                 ("reserved0", _i32), ("x", _vp), ("logits", _vp), ("y", _vp),
                 ("eidx", _vp), ("weights", _vp), ("counts", _vp), ("bounds", _vp), ("rows", _vp),
                 ("pos", _vp), ("xq", _vp), ("dx", _vp), ("gu", _vp), ("h", _vp), ("hq", _vp),
-                ("dh", _vp), ("dm", _vp)]
+                ("dh", _vp), ("dm", _vp), ("combine", _i32), ("reserved1", _i32)]
+
+
+COMBINE_MODES = {"gather": 0, "atomic": 1}   # MOE_COMBINE_GATHER, MOE_COMBINE_ATOMIC
 
 
 class stream_pool_params_t(ctypes.Structure):
@@ -289,12 +292,16 @@ def _dev_ptr(t: Optional[torch.Tensor], dtype, name: str, numel: Optional[int] =
 
 
 def _layer_io(P: dict, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor, layer: int,
-              weights: Optional[torch.Tensor], exports: Optional[Dict[str, torch.Tensor]]) -> moe_layer_io_t:
+              weights: Optional[torch.Tensor], exports: Optional[Dict[str, torch.Tensor]],
+              combine: str = "gather") -> moe_layer_io_t:
     T = x.shape[0]
     io = moe_layer_io_t()
     io.struct_size = ctypes.sizeof(io)
     io.layer = layer
     io.n_tokens = T
+    if combine not in COMBINE_MODES:
+        raise ValueError(f"combine must be one of {sorted(COMBINE_MODES)}")
+    io.combine = COMBINE_MODES[combine]
     io.x = _dev_ptr(x, torch.float32, "x", T * P["d_model"])
     io.logits = _dev_ptr(logits, torch.float32, "logits", T * P["n_experts"])
     io.y = _dev_ptr(y, torch.float32, "y", T * P["d_model"])
@@ -319,9 +326,11 @@ def _layer_io(P: dict, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor, l
 def moe_prefill_run_layer(handle: Handle, x: torch.Tensor, logits: torch.Tensor, y: torch.Tensor,
                           layer: int = -1, weights: Optional[torch.Tensor] = None,
                           stream: Optional[torch.cuda.Stream] = None,
-                          exports: Optional[Dict[str, torch.Tensor]] = None) -> None:
-    """Enqueue one MoE prefill FFN layer on ``stream`` (default: torch's current stream)."""
-    io = _layer_io(handle.params, x, logits, y, layer, weights, exports)
+                          exports: Optional[Dict[str, torch.Tensor]] = None,
+                          combine: str = "gather") -> None:
+    """Enqueue one MoE prefill FFN layer on ``stream`` (default: torch's current stream).
+    combine: "gather" (deterministic, default) or "atomic" (the down GEMM adds into y)."""
+    io = _layer_io(handle.params, x, logits, y, layer, weights, exports, combine)
     s = stream if stream is not None else torch.cuda.current_stream(x.device)
     _check(lib().moe_prefill_run_layer(handle.ptr, ctypes.byref(io), _vp(s.cuda_stream)), handle.ptr)
 
@@ -329,12 +338,13 @@ def moe_prefill_run_layer(handle: Handle, x: torch.Tensor, logits: torch.Tensor,
 def moe_prefill_run_layer_noalloc(d_model: int, d_ff: int, n_experts: int, top_k: int, x: torch.Tensor,
                                   logits: torch.Tensor, y: torch.Tensor, weights: torch.Tensor,
                                   device: int = 0, stream: Optional[torch.cuda.Stream] = None,
-                                  exports: Optional[Dict[str, torch.Tensor]] = None) -> None:
+                                  exports: Optional[Dict[str, torch.Tensor]] = None,
+                                  combine: str = "gather") -> None:
     """One resident layer with no handle and no device allocation: the library's static
     per-device scratch array is the workspace (calls on one device must not overlap)."""
     T = x.shape[0]
     P = dict(d_model=d_model, d_ff=d_ff, n_experts=n_experts, top_k=top_k, max_tokens=max(T, 1))
-    io = _layer_io(P, x, logits, y, -1, weights, exports)
+    io = _layer_io(P, x, logits, y, -1, weights, exports, combine)
     p = _params(d_model, d_ff, n_experts, top_k, max(T, 1), device)
     s = stream if stream is not None else torch.cuda.current_stream(x.device)
     _check(lib().moe_prefill_run_layer_noalloc(ctypes.byref(p), ctypes.byref(io), _vp(s.cuda_stream)))

@@ -27,6 +27,12 @@ struct GemmArgs {
     int a_scale_stride;       // floats per A_scale row (a multiple of the 8-block scale group)
     const uint32_t* fold_flag;  // nonzero: some A scale is outside the range the 16x codes allow
     uint32_t* h_flag;         // gate/up launch: set when an H block scale is outside that range
+    // down launch, atomic combine: y [T, N] += wts[rows[r]] * (row r of the product) for row r
+    // of token rtok[r], fp32 atomic adds (out is then null); null: the product goes to out
+    float* y_add;
+    const int32_t* rows;      // row -> pair t*k + j
+    const int32_t* rtok;      // row -> token
+    const float* wts;         // pair -> router weight
 };
 
 struct LayerLaunch {
@@ -58,6 +64,8 @@ struct LayerLaunch {
     uint8_t* load_dst;        // layer and its pool slot (load_src null: the blob is in place)
     unsigned long long* load_stats;   // [2] experts and bytes loaded (device counters)
     float* h_out;             // optional export of H (nullptr: not written)
+    int combine_atomic = 0;   // 1: the down GEMM adds w * Dm into y with atomics (y zeroed first,
+                              // Dm not stored); the combine launch then only clears the mask
     hipEvent_t* marks;        // optional: kNumKernels + 1 timing events (nullptr: none);
                               // marks[i] before kernel i, marks[kNumKernels] after the last
 };

@@ -900,6 +900,24 @@ __device__ __forceinline__ void grouped_gemm_body(const GemmArgs& g, const GemmI
     }
     if (!wave_on) return;
     const int col = nt * 32 + j32;
+    if (g.y_add) {                        // atomic combine: y[token] += w * row, no Dm
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 8 * gq + 4 * h + i;
+                if (row < nrows) {
+                    const int r = r0 + row;
+                    atomicAdd(g.y_add + (int64_t)g.rtok[r] * N + col, g.wts[g.rows[r]] * acc0[4 * gq + i]);
+                }
+                if (row + 32 < nrows) {
+                    const int r = r0 + row + 32;
+                    atomicAdd(g.y_add + (int64_t)g.rtok[r] * N + col, g.wts[g.rows[r]] * acc1[4 * gq + i]);
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
 #pragma unroll
@@ -1057,7 +1075,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
                        L.rtok);
     const int max_tiles_now = (int)((R + kBM - 1) / kBM) + (L.E < R ? L.E : (int)R);
 
-    GemmArgs gu;
+    GemmArgs gu = {};
     gu.A = L.xq;
     gu.A_scale = L.dx;
     gu.a_scale_stride = scale_stride(L.d);
@@ -1091,7 +1109,11 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     dn.row_src = nullptr;
     dn.q_off = L.d_q_off;
     dn.s_off = L.d_s_off;
-    dn.out = L.dm;
+    dn.out = L.combine_atomic ? nullptr : L.dm;
+    dn.y_add = L.combine_atomic ? L.y : nullptr;
+    dn.rows = L.rows;
+    dn.rtok = L.rtok;
+    dn.wts = L.wts;
     dn.hq = nullptr;
     dn.dh = nullptr;
     dn.h_out = nullptr;
@@ -1101,6 +1123,10 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     dn.fold_flag = gu.h_flag;
     dn.h_flag = nullptr;
     mark(L, kGemmDown, st);
+    if (L.combine_atomic) {               // the atomic combine adds into a zeroed y
+        const hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(L.y), (int64_t)L.T * L.d, 0u, st);
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(k_gemm_down, dim3(nblk(dn.N / 32, 4) * tiles8), dim3(kGemmThreads), 0, st, dn);
     mark(L, kCombine, st);
     return hipGetLastError();
@@ -1110,6 +1136,11 @@ hipError_t launch_combine(const LayerLaunch& L, hipStream_t st)
 {
     const int64_t work = (int64_t)L.T * (L.d / 4);
     const int64_t mw = (int64_t)mask_words(L.E, L.W);    // the mask and the scale flags
+    if (L.combine_atomic) {               // y is complete: only clear the grouping state
+        const hipError_t e = launch_fill_u32(L.mask, mw, 0u, st);
+        mark(L, kNumKernels, st);
+        return e;
+    }
     hipLaunchKernelGGL(k_combine, dim3(nblk(work > mw ? work : mw, 256)), dim3(256), 0, st, L.dm,
                        L.wts, L.pos, L.T, L.k, L.d, L.y, L.mask, mw);
     mark(L, kNumKernels, st);

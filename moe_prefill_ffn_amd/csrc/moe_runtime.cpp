@@ -699,12 +699,27 @@ void moe_prefill_destroy(moe_prefill_t* h)
     delete h;
 }
 
+// Whether the combine mode of a layer call is valid (else why not).
+static bool combine_ok(const moe_layer_io_t& io, std::string* why)
+{
+    if (io.combine != MOE_COMBINE_GATHER && io.combine != MOE_COMBINE_ATOMIC) {
+        *why = "combine must be MOE_COMBINE_GATHER (0) or MOE_COMBINE_ATOMIC (1)";
+        return false;
+    }
+    if (io.combine == MOE_COMBINE_ATOMIC && io.dm) {
+        *why = "dm cannot be exported with MOE_COMBINE_ATOMIC (the down GEMM adds into y, Dm is not stored)";
+        return false;
+    }
+    return true;
+}
+
 int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* stream)
 {
     if (!h) return fail(nullptr, MOE_EINVAL, "null handle");
     moe_layer_io_t io;
     std::string why;
     if (!read_struct(io_in, &io, &why)) return fail(h, MOE_EINVAL, why);
+    if (!combine_ok(io, &why)) return fail(h, MOE_EINVAL, why);
     const int T = io.n_tokens;
     if (T < 0 || T > h->Tmax) return fail(h, MOE_EINVAL, "n_tokens out of [0, max_tokens]");
     if (T == 0) return MOE_OK;
@@ -796,6 +811,7 @@ int moe_prefill_run_layer(moe_prefill_t* h, const moe_layer_io_t* io_in, void* s
     bind_layer(LL, h->ws, h->L, h->B);
     LL.h_out = io.h;
     LL.gu = io.gu;
+    LL.combine_atomic = io.combine == MOE_COMBINE_ATOMIC;
     LL.marks = nullptr;
     std::array<hipEvent_t, kNumKernels + 1> tset{};
     if (h->timing) {
@@ -875,6 +891,7 @@ int moe_prefill_run_layer_noalloc(const moe_prefill_params_t* pin, const moe_lay
     std::string why;
     if (!read_struct(pin, &p, &why)) return fail(nullptr, MOE_EINVAL, why);
     if (!read_struct(io_in, &io, &why)) return fail(nullptr, MOE_EINVAL, why);
+    if (!combine_ok(io, &why)) return fail(nullptr, MOE_EINVAL, why);
     const int T = io.n_tokens;
     if (T < 0) return fail(nullptr, MOE_EINVAL, "noalloc: n_tokens < 0");
     p.max_tokens = T > 0 ? T : 1;                     // the workspace is laid out for this T
@@ -920,6 +937,7 @@ int moe_prefill_run_layer_noalloc(const moe_prefill_params_t* pin, const moe_lay
     bind_layer(LL, ws, L, B);
     LL.h_out = io.h;
     LL.gu = io.gu;
+    LL.combine_atomic = io.combine == MOE_COMBINE_ATOMIC;
     LL.marks = nullptr;
     e = launch_layer(LL, st);
     if (e == hipSuccess) e = launch_combine(LL, st);

@@ -5,16 +5,19 @@
  * versioned C API structures" and "compatibility of an executable built against
  * the previous public API" (stable-diffusion.cpp #1905, "Verification"); this
  * client carries the first published layouts of the structs that have grown
- * since (stream_pool_params_v1, moe_stats_v1) and calls the library with them.
+ * since (stream_pool_params_v1, moe_stats_v1, moe_layer_io_v1) and calls the
+ * library with them.
  *
  *   abi_client layout         sizeof / offsetof of every public struct (JSON)
  *   abi_client host           host-only calls with current, undersized and
  *                             oversized structs (JSON); needs no GPU
  *   abi_client gpu DIR T d f E k
  *                             one resident layer and a 2-layer pool through
- *                             the old struct layouts; inputs x.bin, logits.bin,
- *                             blob.bin from DIR, outputs y_res.bin, y_pool0.bin,
- *                             y_pool1.bin into DIR (JSON of return codes and
+ *                             the old struct layouts, and one resident layer
+ *                             with the atomic combine through the current one;
+ *                             inputs x.bin, logits.bin, blob.bin from DIR,
+ *                             outputs y_res.bin, y_pool0.bin, y_pool1.bin,
+ *                             y_atomic.bin into DIR (JSON of return codes and
  *                             counters on stdout)
  */
 #include <stddef.h>
@@ -38,6 +41,30 @@ typedef struct stream_pool_params_v1 {
     int32_t eff_slots, eff_depth, eff_residents, warnings;
     int32_t reserved0;
 } stream_pool_params_v1;
+
+typedef struct moe_layer_io_v1 {
+    uint32_t struct_size;
+    int32_t layer;
+    const void* weights_dev;
+    int32_t n_tokens;
+    int32_t reserved0;
+    const float* x;
+    const float* logits;
+    float* y;
+    int32_t* eidx;
+    float* weights;
+    int32_t* counts;
+    int32_t* bounds;
+    int32_t* rows;
+    int32_t* pos;
+    int8_t* xq;
+    float* dx;
+    float* gu;
+    float* h;
+    int8_t* hq;
+    float* dh;
+    float* dm;
+} moe_layer_io_v1;
 
 typedef struct moe_stats_v1 {
     uint32_t struct_size;
@@ -69,6 +96,7 @@ static int layout(void)
     FIELD(moe_layer_io_t, rows); FIELD(moe_layer_io_t, pos); FIELD(moe_layer_io_t, xq);
     FIELD(moe_layer_io_t, dx); FIELD(moe_layer_io_t, gu); FIELD(moe_layer_io_t, h);
     FIELD(moe_layer_io_t, hq); FIELD(moe_layer_io_t, dh); FIELD(moe_layer_io_t, dm);
+    FIELD(moe_layer_io_t, combine); FIELD(moe_layer_io_t, reserved1);
     END();
     BEGIN(stream_pool_params_t);
     FIELD(stream_pool_params_t, struct_size); FIELD(stream_pool_params_t, n_layers);
@@ -113,8 +141,8 @@ static int layout(void)
     FIELD(moe_kernel_times_t, struct_size); FIELD(moe_kernel_times_t, n_kernels);
     FIELD(moe_kernel_times_t, launches); FIELD(moe_kernel_times_t, total_ms);
     END();
-    printf(", \"v1_sizes\": {\"stream_pool_params_v1\": %zu, \"moe_stats_v1\": %zu}",
-           sizeof(stream_pool_params_v1), sizeof(moe_stats_v1));
+    printf(", \"v1_sizes\": {\"stream_pool_params_v1\": %zu, \"moe_stats_v1\": %zu, \"moe_layer_io_v1\": %zu}",
+           sizeof(stream_pool_params_v1), sizeof(moe_stats_v1), sizeof(moe_layer_io_v1));
     printf(", \"abi_version\": %d}\n", MOE_PREFILL_ABI_VERSION);
     return 0;
 }
@@ -268,7 +296,8 @@ static int gpu(const char* dir, int T, int d, int f, int E, int k)
     CK(hipMemcpy(dl, lg, nl, hipMemcpyHostToDevice));
     CK(hipMemcpy(dblob, blob, nb, hipMemcpyHostToDevice));
 
-    moe_layer_io_t io;
+    /* the first published layer layout: no combine field, so the default gather */
+    moe_layer_io_v1 io;
     memset(&io, 0, sizeof io);
     io.struct_size = sizeof io;
     io.layer = -1;
@@ -277,9 +306,24 @@ static int gpu(const char* dir, int T, int d, int f, int E, int k)
     io.x = dx;
     io.logits = dl;
     io.y = y;
-    const int rc_res = moe_prefill_run_layer(h, &io, NULL);
+    const int rc_res = moe_prefill_run_layer(h, (const moe_layer_io_t*)&io, NULL);
     CK(hipDeviceSynchronize());
     if (write_dev(dir, "y_res.bin", y, nx)) return 2;
+
+    /* the current layout with the atomic combine */
+    moe_layer_io_t ioa;
+    memset(&ioa, 0, sizeof ioa);
+    ioa.struct_size = sizeof ioa;
+    ioa.layer = -1;
+    ioa.weights_dev = dblob;
+    ioa.n_tokens = T;
+    ioa.x = dx;
+    ioa.logits = dl;
+    ioa.y = y;
+    ioa.combine = MOE_COMBINE_ATOMIC;
+    const int rc_atomic = moe_prefill_run_layer(h, &ioa, NULL);
+    CK(hipDeviceSynchronize());
+    if (write_dev(dir, "y_atomic.bin", y, nx)) return 2;
 
     /* a two-layer pool configured through the first published stream-pool layout */
     void* pinned[2];
@@ -299,11 +343,11 @@ static int gpu(const char* dir, int T, int d, int f, int E, int k)
     int rc_l0 = -100, rc_l1 = -100;
     io.weights_dev = NULL;
     io.layer = 0;
-    rc_l0 = moe_prefill_run_layer(h, &io, NULL);
+    rc_l0 = moe_prefill_run_layer(h, (const moe_layer_io_t*)&io, NULL);
     CK(hipDeviceSynchronize());
     if (write_dev(dir, "y_pool0.bin", y, nx)) return 2;
     io.layer = 1;
-    rc_l1 = moe_prefill_run_layer(h, &io, NULL);
+    rc_l1 = moe_prefill_run_layer(h, (const moe_layer_io_t*)&io, NULL);
     CK(hipDeviceSynchronize());
     if (write_dev(dir, "y_pool1.bin", y, nx)) return 2;
 
@@ -311,11 +355,11 @@ static int gpu(const char* dir, int T, int d, int f, int E, int k)
     memset(&st, 0xff, sizeof st);
     st.struct_size = sizeof st;
     const int rc_stats = moe_prefill_get_stats(h, (moe_stats_t*)&st);
-    printf("{\"rc_create\": %d, \"rc_resident\": %d, \"rc_pool\": %d, \"eff_slots\": %d, \"eff_depth\": %d, "
+    printf("{\"rc_create\": %d, \"rc_resident\": %d, \"rc_atomic\": %d, \"rc_pool\": %d, \"eff_slots\": %d, \"eff_depth\": %d, "
            "\"eff_residents\": %d, \"pool_struct_size_kept\": %u, \"rc_layer0\": %d, \"rc_layer1\": %d, "
            "\"rc_stats\": %d, \"stats_struct_size_kept\": %u, \"layers_run\": %llu, \"prefetch_queued\": %llu, "
            "\"prefetch_activated\": %llu, \"sync_loads\": %llu, \"bytes_h2d\": %llu}\n",
-           rc_create, rc_res, rc_pool, sp.eff_slots, sp.eff_depth, sp.eff_residents, sp.struct_size, rc_l0, rc_l1,
+           rc_create, rc_res, rc_atomic, rc_pool, sp.eff_slots, sp.eff_depth, sp.eff_residents, sp.struct_size, rc_l0, rc_l1,
            rc_stats, st.struct_size, (unsigned long long)st.layers_run, (unsigned long long)st.prefetch_queued,
            (unsigned long long)st.prefetch_activated, (unsigned long long)st.sync_loads,
            (unsigned long long)st.bytes_h2d);

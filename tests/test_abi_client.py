@@ -72,6 +72,7 @@ def test_first_published_layouts_are_prefixes_of_the_current_ones(client):
     v1 = lay["v1_sizes"]
     assert v1["stream_pool_params_v1"] == lay["stream_pool_params_t"]["fields"]["active_only"]
     assert v1["moe_stats_v1"] == lay["moe_stats_t"]["fields"]["sparse_loads"]
+    assert v1["moe_layer_io_v1"] == lay["moe_layer_io_t"]["fields"]["combine"]
 
 
 def test_current_undersized_and_oversized_structs(client):
@@ -112,13 +113,15 @@ def test_c_client_runs_a_layer_and_a_pool_through_old_struct_layouts(tmp_path):
     lg.tofile(tmp_path / "logits.bin")
     blob.tofile(tmp_path / "blob.bin")
     r = _run(exe, "gpu", tmp_path, w.T, w.d, w.f, w.E, w.k, timeout=110)
-    assert r["rc_create"] == 0 and r["rc_resident"] == 0
+    assert r["rc_create"] == 0 and r["rc_resident"] == 0 and r["rc_atomic"] == 0
     assert r["rc_pool"] == 0 and (r["eff_slots"], r["eff_depth"], r["eff_residents"]) == (2, 1, 0)
     assert r["rc_layer0"] == 0 and r["rc_layer1"] == 0 and r["rc_stats"] == 0
     assert r["pool_struct_size_kept"] == 64 and r["stats_struct_size_kept"] == 72
-    assert r["layers_run"] == 3 and r["sync_loads"] == 1 and r["prefetch_activated"] == 1
+    assert r["layers_run"] == 4 and r["sync_loads"] == 1 and r["prefetch_activated"] == 1
     y_res = np.fromfile(tmp_path / "y_res.bin", dtype=np.float32).reshape(w.T, w.d)
     ref = oracle.layer(x, lg, w.k, ex, w.f)
     assert_close("C client y", y_res, ref["y"])
     for name in ("y_pool0.bin", "y_pool1.bin"):
         assert_equal(name, np.fromfile(tmp_path / name, dtype=np.float32).reshape(w.T, w.d), y_res)
+    assert_close("C client y, atomic combine",
+                 np.fromfile(tmp_path / "y_atomic.bin", dtype=np.float32).reshape(w.T, w.d), ref["y"])

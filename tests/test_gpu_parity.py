@@ -4,6 +4,8 @@ full, edge cases (ragged T, single token, one expert, E not a multiple of 64,
 partial K stages, empty experts, ties, zero input), and the large skewed /
 biased shapes on sampled rows and tokens in the bench's launch configuration.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -11,7 +13,7 @@ import torch
 import moe_prefill_ffn_amd as mp
 import oracle
 import workload as wl
-from gpu_helpers import (ExpertCache, assert_close, assert_equal, check_full_parity,
+from gpu_helpers import (EXPORT_SHAPES, ExpertCache, assert_close, assert_equal, check_full_parity,
                          check_sampled_parity, host_blob, make_handle, run_layer_gpu, say)
 
 pytestmark = pytest.mark.gpu
@@ -296,16 +298,16 @@ def test_lent_workspace():
     assert ei.value.code == mp.MOE_EINVAL
 
 
-def _sampled_case(name, n_tok=24, seed=0):
+def _sampled_case(name, n_tok=24, seed=0, combine="gather"):
     w = wl.WORKLOADS[name]
-    say(f"[case] {w.name} layer 0 (sampled)")
+    say(f"[case] {w.name} layer 0 (sampled, {combine} combine)")
     x = wl.layer_activations(w, 0)
     lg = wl.layer_logits(w, 0)
     blob_ex = ExpertCache(w, 0, keep=False)
     blob = host_blob(w, blob_ex).cuda()
     h = make_handle(w)
-    g = run_layer_gpu(h, w, x, lg, blob, exports=("eidx", "weights", "counts", "bounds", "rows", "pos",
-                                                  "xq", "dx", "hq", "dh", "dm"))
+    ex = ("eidx", "weights", "counts", "bounds", "rows", "pos", "xq", "dx", "hq", "dh")
+    g = run_layer_gpu(h, w, x, lg, blob, exports=ex + (("dm",) if combine == "gather" else ()), combine=combine)
     h.close()
     del blob
     torch.cuda.empty_cache()
@@ -329,6 +331,61 @@ def test_skewed_large_shape_sampled():
     w, g, ref = _sampled_case("skew", n_tok=16)
     check_sampled_parity(w, g, ref)
     assert ref["counts"].max() > 1000 and (ref["counts"] == 0).sum() > 10
+
+
+def test_skewed_large_shape_sampled_atomic_combine():
+    w, g, ref = _sampled_case("skew", n_tok=16, seed=1, combine="atomic")
+    check_sampled_parity(w, g, ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "resident"])
+def test_atomic_combine_matches_the_oracle(name):
+    """MOE_COMBINE_ATOMIC: every stage up to Dm is the gather mode's (bit-exact against
+    the oracle), y is within the combine's tolerance of the oracle, and repeated runs
+    agree with each other and with the gather mode to within rounding (the order of
+    the atomic adds varies)."""
+    w = wl.WORKLOADS[name]
+    say(f"[case] atomic combine {name}")
+    x = wl.layer_activations(w, 0)
+    lg = wl.layer_logits(w, 0)
+    ex = ExpertCache(w, 0)
+    blob = host_blob(w, ex).cuda()
+    h = make_handle(w)
+    names = tuple(n for n in EXPORT_SHAPES if n != "dm")
+    g = run_layer_gpu(h, w, x, lg, blob, exports=names, combine="atomic")
+    ref = oracle.layer(x, lg, w.k, ex, w.f)
+    check_full_parity(w, g, ref)
+    g2 = run_layer_gpu(h, w, x, lg, blob, exports=(), combine="atomic")
+    y_gather = run_layer_gpu(h, w, x, lg, blob, exports=())["y"]
+    h.close()
+    # Both modes sum the same fp32 products w * Dm of each token's k rows; the gather
+    # as an fma chain in slot order, the atomic mode as rounded products added in any
+    # order.  Each result is within (k + 1) roundings of sum |w * Dm| of the exact sum,
+    # so two results differ by at most 2 (k + 1) 2^-24 sum |w * Dm| per element.
+    pos = ref["pos"].reshape(w.T, w.k)
+    mag = np.einsum("tj,tjc->tc", np.abs(ref["w"]), np.abs(ref["dm"][pos]))
+    bound = 2 * (w.k + 1) * 2.0 ** -24 * mag * 1.001
+    for name, other in (("repeat", g2["y"]), ("gather", y_gather)):
+        diff = np.abs(other.astype(np.float64) - g["y"])
+        assert (diff <= bound).all(), (name, diff.max(), bound[np.unravel_index(diff.argmax(), diff.shape)])
+
+
+def test_atomic_combine_refuses_a_dm_export_and_unknown_modes():
+    w = wl.WORKLOADS["tiny"]
+    x = torch.from_numpy(wl.layer_activations(w, 0)).cuda()
+    lg = torch.from_numpy(wl.layer_logits(w, 0)).cuda()
+    blob = host_blob(w, ExpertCache(w, 0)).cuda()
+    h = make_handle(w)
+    y = torch.empty(w.T, w.d, device="cuda")
+    dm = torch.empty(w.T * w.k, w.d, device="cuda")
+    with pytest.raises(mp.MoePrefillError) as ei:
+        mp.moe_prefill_run_layer(h, x, lg, y, weights=blob, exports={"dm": dm}, combine="atomic")
+    assert ei.value.code == mp.MOE_EINVAL and "dm" in str(ei.value)
+    io = mp._layer_io(h.params, x, lg, y, -1, blob, None)
+    io.combine = 7
+    rc = mp.lib().moe_prefill_run_layer(h.ptr, ctypes.byref(io), None)   # rejected before any launch
+    assert rc == mp.MOE_EINVAL and b"combine" in mp.lib().moe_prefill_last_error(h.ptr)
+    h.close()
 
 
 @pytest.mark.parametrize("name", ["tiny", "resident"])

@@ -75,6 +75,23 @@ def test_rolling_window_depth1_two_slots(tiny5):
     h.close()
 
 
+def test_streamed_atomic_combine_matches_resident_within_rounding(tiny5):
+    """The atomic combine on pool slots (prefetched and loaded): the same y as the
+    resident gather to within the rounding of a different order of the k adds."""
+    h = make_handle(tiny5.w)
+    _configure(h, tiny5, prefetch_depth=1, resident_layers=1, requested_slots=3)
+    outs = []
+    for l in range(tiny5.n):
+        y = torch.full((tiny5.w.T, tiny5.w.d), float("nan"), device="cuda")
+        mp.moe_prefill_run_layer(h, tiny5.x[l], tiny5.lg[l], y, layer=l, combine="atomic")
+        outs.append((l, y))
+    torch.cuda.synchronize()
+    for l, y in outs:
+        ref = tiny5.ref[l].astype(np.float64)
+        assert np.abs(y.cpu().numpy() - ref).max() <= 1e-5 * np.abs(ref).max(), l
+    h.close()
+
+
 def test_depth0_is_load_then_compute(tiny5):
     h = make_handle(tiny5.w)
     plan = _configure(h, tiny5, prefetch_depth=0, resident_layers=0)
