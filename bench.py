@@ -160,9 +160,12 @@ def stack_leg(mp, wl, torch, dev, key: str, passes: int) -> dict:
         t_copy = min(t_copy, time.perf_counter() - t0)
     del dst
     torch.cuda.empty_cache()
-    for l in range(w.n_layers):            # first (cold) pass
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for l in range(w.n_layers):            # first (cold) pass: nothing prefetched yet
         mp.moe_prefill_run_layer(h, xs[l], lgs[l], y, layer=l)
     torch.cuda.synchronize()
+    t_cold = time.perf_counter() - t0
     s0 = mp.moe_prefill_get_stats(h)
     t_pass = []
     for _ in range(passes):
@@ -182,6 +185,7 @@ def stack_leg(mp, wl, torch, dev, key: str, passes: int) -> dict:
         "residents": plan["residents"], "streamed_layers": streamed,
         "tokens_per_s_per_pass": round(w.T / t_wall, 1), "ms_per_pass": round(t_wall * 1e3, 3),
         "ms_per_pass_all": [round(t * 1e3, 3) for t in t_pass],
+        "cold_pass": {"ms": round(t_cold * 1e3, 3), "tokens_per_s": round(w.T / t_cold, 1)},
         "h2d_GB_per_pass": round(moved / 1e9, 3), "h2d_GBs_achieved": round(moved / t_wall / 1e9, 2),
         "pcie_h2d_GBs_measured": round(pcie / 1e9, 2),
         "pcie_roofline_frac": round((moved / pcie) / t_wall, 4) if pcie > 0 else None,
@@ -784,9 +788,12 @@ def main() -> int:
         plan = mp.stream_pool_configure(hs, blobs, prefetch_depth=ws.stream.depth,
                                         resident_layers=ws.stream.residents,
                                         requested_slots=ws.stream.slots)
-        for l in range(ws.n_layers):       # first (cold) pass
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for l in range(ws.n_layers):       # first (cold) pass: nothing prefetched yet
             mp.moe_prefill_run_layer(hs, xs[l], lgs[l], ys, layer=l)
         torch.cuda.synchronize()
+        t_cold = time.perf_counter() - t0
         s0 = mp.moe_prefill_get_stats(hs)
         t0 = time.perf_counter()
         for _ in range(args.stream_passes):
@@ -801,6 +808,7 @@ def main() -> int:
             "workload": ws.name, "layers": ws.n_layers, "slots": plan["slots"], "depth": plan["depth"],
             "tokens_per_s_per_pass": round(ws.T / t_wall, 1),
             "ms_per_pass": round(t_wall * 1e3, 3), "ms_per_layer": round(t_wall * 1e3 / ws.n_layers, 3),
+            "cold_pass": {"ms": round(t_cold * 1e3, 3), "tokens_per_s": round(ws.T / t_cold, 1)},
             "h2d_GBs_achieved": round(moved / t_wall / 1e9, 2),
             "pcie_h2d_GBs_measured": round(ws.n_layers * lb / t_copy / 1e9, 2),
             "copy_ms_per_pass": round(t_copy * 1e3, 3), "compute_ms_per_pass": round(t_comp * 1e3, 3),
