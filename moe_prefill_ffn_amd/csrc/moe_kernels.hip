@@ -198,21 +198,38 @@ __device__ __forceinline__ bool scale_outside_fold_range(float d)
 }
 
 // x is a flat array of n_blocks 32-float blocks (a row-major [rows, K] matrix
-// with K % 32 == 0); 8 lanes per block, 4 values per lane.
-// block blk = row * nbk + b; its scale goes to scale[row * stride + b]
-__device__ __forceinline__ void quant_block8(const float* __restrict__ x, int64_t blk, int nbk,
-                                             int stride, int8_t* __restrict__ q,
-                                             float* __restrict__ scale, uint32_t* __restrict__ flag)
+// with K % 32 == 0); 8 lanes per block, 4 values per lane.  A wave takes
+// kQuantBlocksPerWave consecutive blocks: its 8-lane group g the blocks b0 + g,
+// + 8, + 16, + 24, so each of the four loads reads 1 KiB of contiguous X and all
+// four are in flight together.  Block blk = row * nbk + b; its scale goes to
+// scale[row * stride + b].  n_blocks < 2^31 (T * d / 32 <= 2^21 * 512).
+constexpr int kQuantBlocksPerWave = 32;
+
+__device__ __forceinline__ void quant_blocks_of_wave(const float* __restrict__ x, int64_t b0,
+                                                     int64_t n_blocks, int nbk, int stride,
+                                                     int8_t* __restrict__ q, float* __restrict__ scale,
+                                                     uint32_t* __restrict__ flag)
 {
     const int sub = threadIdx.x & 7;
-    const float4 v = *reinterpret_cast<const float4*>(x + blk * 32 + sub * 4);
-    float d;
-    const uint32_t packed = q8_block_of8(v, &d);
-    *reinterpret_cast<uint32_t*>(q + blk * 32 + sub * 4) = packed;
-    if (sub == 0) {
-        const int64_t row = blk / nbk;
-        scale[row * stride + (blk - row * nbk)] = d;
-        if (scale_outside_fold_range(d)) atomicOr(flag, 1u);
+    constexpr int kN = kQuantBlocksPerWave / 8;
+    float4 v[kN];
+#pragma unroll
+    for (int j = 0; j < kN; ++j) {                // clamped: a block past the end is loaded, not used
+        const int64_t blk = b0 + 8 * j < n_blocks ? b0 + 8 * j : n_blocks - 1;
+        v[j] = *reinterpret_cast<const float4*>(x + blk * 32 + sub * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < kN; ++j) {
+        const int64_t blk = b0 + 8 * j;
+        if (blk >= n_blocks) break;               // uniform over the 8-lane group
+        float d;
+        const uint32_t packed = q8_block_of8(v[j], &d);
+        *reinterpret_cast<uint32_t*>(q + blk * 32 + sub * 4) = packed;
+        if (sub == 0) {
+            const uint32_t row = (uint32_t)blk / (uint32_t)nbk;
+            scale[(int64_t)row * stride + ((uint32_t)blk - row * (uint32_t)nbk)] = d;
+            if (scale_outside_fold_range(d)) atomicOr(flag, 1u);
+        }
     }
 }
 
@@ -243,9 +260,9 @@ __global__ __launch_bounds__(256) void k_route_quant(const float* __restrict__ l
             route_token<kRouteKeys>(logits, t, E, k, eidx, wts, mask, W, zsel[wave]);
         return;
     }
-    const int64_t g = (int64_t)(blockIdx.x - n_route) * 256 + threadIdx.x;
-    const int64_t blk = g >> 3;
-    if (blk < n_blocks) quant_block8(x, blk, nbk, dx_stride, xq, dx, x_flag);   // whole 8-lane groups together
+    const int64_t wave = ((int64_t)(blockIdx.x - n_route) * 256 + threadIdx.x) >> 6;
+    const int64_t b0 = wave * kQuantBlocksPerWave + ((threadIdx.x & 63) >> 3);
+    if (b0 < n_blocks) quant_blocks_of_wave(x, b0, n_blocks, nbk, dx_stride, xq, dx, x_flag);
 }
 
 // ---------------------------------------------------------------- group ---
@@ -1059,7 +1076,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     const int n_route = L.E <= kRankMaxE ? L.T : (int)nblk(L.T, 4);   // routing workgroups
     const int64_t xblocks = (int64_t)L.T * (L.d / 32);
     mark(L, kRouteQuant, st);
-    hipLaunchKernelGGL(k_route_quant, dim3(n_route + nblk(xblocks * 8, 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_route_quant, dim3(n_route + nblk(xblocks, 4 * kQuantBlocksPerWave)), dim3(256), 0, st,
                        L.logits, L.T, L.E, L.k, L.eidx, L.wts, L.mask, L.W, n_route, L.x, xblocks,
                        L.d / 32, scale_stride(L.d), L.xq, L.dx, L.mask + (int64_t)L.E * L.W);
     mark(L, kGroup, st);
