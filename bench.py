@@ -602,14 +602,15 @@ def micro_leg(torch, dev) -> dict:
         valu[name] = round(simd_cycles(r, iters) / (4 * 64), 3)   # SIMD cycles per wave64 instruction
     out["valu_cycles_per_wave_instr"] = valu
     # co-execution: SIMD cycles per loop iteration of the single-kind loops (per wave and
-    # iteration: 64 fmas, 64 converts, four int8 MFMAs, two scale-product MFMAs) beside the
-    # loops that issue both kinds (two int8 MFMAs + 64 fmas, two int8 MFMAs + 64 converts,
-    # one scale-product MFMA + 64 fmas), none depending on the other
+    # iteration: 64 fmas, 64 converts, four int8 MFMAs, two scale-product MFMAs taken at once
+    # or chained through C) beside the loops that issue both kinds (two int8 MFMAs + 64 fmas
+    # or converts; one scale-product MFMA + 64 fmas with its result taken at once, or
+    # chained through C beside 64 fmas or converts), the VALU work independent of the MFMAs
     coexec = {}
     for wps in (1, 4):
         row = {}
-        for name in ("valu_fma", "valu_cvt", "mfma_i8", "mfma_f32_scale", "overlap_indep", "overlap_cvt",
-                     "overlap_scale_fma"):
+        for name in ("valu_fma", "valu_cvt", "mfma_i8", "mfma_f32_scale", "mfma_f32_chain", "overlap_indep",
+                     "overlap_cvt", "overlap_scale_fma", "overlap_scale_chain", "overlap_scale_cvt"):
             r = micro.block(name, 20000, n_cu, wps)
             row[name] = round(simd_cycles(r, 20000), 1)
         coexec[f"{wps}w"] = row

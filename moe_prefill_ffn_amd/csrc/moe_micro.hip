@@ -25,7 +25,11 @@
 //   mfma_f32_scale   v_mfma_f32_32x32x1_2b_f32 alone (the scale-product MFMA)
 //   overlap_cvt / overlap_mul / overlap_fma16   two int8 MFMAs beside 64 independent
 //                    converts, 64 multiplies, or only 16 fmas
-//   overlap_scale_fma  one scale-product MFMA beside 64 independent fmas
+//   overlap_scale_fma  one scale-product MFMA beside 64 independent fmas, its result
+//                    taken at once (the wave waits for it)
+//   overlap_scale_chain / overlap_scale_cvt  one scale-product MFMA chained through
+//                    its C operand (no wave waits for it) beside 64 fmas / converts
+//   mfma_f32_chain   two scale-product MFMAs chained through C, nothing else
 //   pipe_cvt_fma     cvt_fma_mscale with the epilogue one block behind the MFMAs
 //                    (the MFMAs of block b+1 issue before the VALU work of block b)
 //
@@ -169,6 +173,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
             }
             continue;
         }
+        if (kTest == 15 || kTest == 16) {   // the scale-product MFMA chained through its C operand
+            // (no wave ever waits for its result) beside 64 independent fmas / converts
+            touchf(dxv);
+            touchf(dw);
+            tp = __builtin_amdgcn_mfma_f32_32x32x1f32(dxv, dw, tp, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (kTest == 15) {
+                    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc0[i]) : "v"(dxr[i]), "v"(dw));
+                    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc1[i]) : "v"(dxr[16 + i]), "v"(dw));
+                    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc0[i]) : "v"(dxr[16 + i]), "v"(dxv));
+                    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(acc1[i]) : "v"(dxr[i]), "v"(dxv));
+                } else {
+                    asm volatile("v_cvt_f32_i32 %0, %1" : "=v"(acc0[i]) : "v"(m2[i]));
+                    asm volatile("v_cvt_f32_i32 %0, %1" : "=v"(acc1[i]) : "v"(m3[i]));
+                    asm volatile("v_cvt_f32_i32 %0, %1" : "=v"(dxr[i]) : "v"(m2[i]));
+                    asm volatile("v_cvt_f32_i32 %0, %1" : "=v"(dxr[16 + i]) : "v"(m3[i]));
+                }
+            }
+            continue;
+        }
+        if (kTest == 17) {           // the scale-product MFMA alone, chained through C
+            touchf(dxv);
+            touchf(dw);
+            tp = __builtin_amdgcn_mfma_f32_32x32x1f32(dxv, dw, tp, 0, 0, 0);
+            t2 = __builtin_amdgcn_mfma_f32_32x32x1f32(dw, dxv, t2, 0, 0, 0);
+            continue;
+        }
         if (kTest == 8) {            // MFMAs beside independent VALU work
             m0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b, m0, 0, 0, 0);
             m1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b, m1, 0, 0, 0);
@@ -282,11 +314,12 @@ typedef struct moe_micro_result {
 
 // test: 0 mfma_i8, 1 cvt_fma_mscale, 2 cvt_fma_vscale, 3 sub_fma_vscale, 4 sub_fma_mscale,
 // 5 valu_fma, 6 valu_cvt, 7 valu_sub, 8 overlap_indep, 9 pipe_cvt_fma, 10 mfma_f32_scale,
-// 11 overlap_cvt, 12 overlap_fma16, 13 overlap_mul, 14 overlap_scale_fma.  blocks_per_cu workgroups of 256 threads on each of
+// 11 overlap_cvt, 12 overlap_fma16, 13 overlap_mul, 14 overlap_scale_fma, 15 overlap_scale_chain,
+// 16 overlap_scale_cvt, 17 mfma_f32_chain.  blocks_per_cu workgroups of 256 threads on each of
 // n_cu compute units.  Returns 0 or a negative HIP error.
 int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_per_cu, moe_micro_result_t* res)
 {
-    if (!res || iters < 1 || n_cu < 1 || blocks_per_cu < 1 || test < 0 || test > 14) return -1;
+    if (!res || iters < 1 || n_cu < 1 || blocks_per_cu < 1 || test < 0 || test > 17) return -1;
     MicroOut* d_out = nullptr;
     hipEvent_t e0, e1;
     if (hipMalloc(&d_out, sizeof(MicroOut)) != hipSuccess) return -2;
@@ -310,7 +343,10 @@ int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_pe
     case 11: hipLaunchKernelGGL(k_block<11>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     case 12: hipLaunchKernelGGL(k_block<12>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     case 13: hipLaunchKernelGGL(k_block<13>, grid, blk, 0, nullptr, iters, 3, d_out); break;
-    default: hipLaunchKernelGGL(k_block<14>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 14: hipLaunchKernelGGL(k_block<14>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 15: hipLaunchKernelGGL(k_block<15>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 16: hipLaunchKernelGGL(k_block<16>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    default: hipLaunchKernelGGL(k_block<17>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     }
     (void)hipEventRecord(e1, nullptr);
     hipError_t e = hipEventSynchronize(e1);
@@ -326,12 +362,12 @@ int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_pe
     res->ms = ms;
     res->cycles_per_wave = (double)h.cycles / waves;
     res->clock_ghz = h.rt ? (double)h.cycles / ((double)h.rt / 100e6) / 1e9 : 0.0;
-    // MFMA tests: MACs per iteration per wave (x2 ops); the VALU-only tests count none
-    // MFMA tests: int8 MACs per iteration per wave (x2 ops); mfma_f32_scale counts its fp32
-    // products (2 x 2048 per iteration); the VALU-only tests count none
+    // MFMA tests: int8 MACs per iteration per wave (x2 ops); the scale-product tests count
+    // their fp32 products (2048 per MFMA); the VALU-only tests count none
     const double macs = test == 0 ? 4.0 * 32768.0
                       : test == 10 ? 2.0 * 2048.0
-                      : test == 14 ? 2048.0
+                      : (test == 14 || test == 15 || test == 16) ? 2048.0
+                      : test == 17 ? 2.0 * 2048.0
                       : ((test <= 4 || (test >= 8 && test != 10)) ? 2.0 * 32768.0 : 0.0);
     res->work = 2.0 * macs * (double)iters * waves;
     return 0;

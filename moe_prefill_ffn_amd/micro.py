@@ -27,7 +27,10 @@ BLOCK_TESTS = {
     "overlap_cvt": 11,     # two int8 MFMAs beside 64 independent converts
     "overlap_fma16": 12,   # two int8 MFMAs beside 16 independent fmas
     "overlap_mul": 13,     # two int8 MFMAs beside 64 independent multiplies
-    "overlap_scale_fma": 14,  # one scale-product MFMA beside 64 independent fmas
+    "overlap_scale_fma": 14,  # one scale-product MFMA beside 64 independent fmas (result taken at once)
+    "overlap_scale_chain": 15,  # one scale-product MFMA chained through C beside 64 fmas
+    "overlap_scale_cvt": 16,    # one scale-product MFMA chained through C beside 64 converts
+    "mfma_f32_chain": 17,       # two scale-product MFMAs chained through C, nothing else
 }
 
 
