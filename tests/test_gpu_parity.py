@@ -370,6 +370,51 @@ def test_atomic_combine_matches_the_oracle(name):
         assert (diff <= bound).all(), (name, diff.max(), bound[np.unravel_index(diff.argmax(), diff.shape)])
 
 
+def test_atomic_combine_captured_in_a_hip_graph():
+    """The atomic combine's extra launches (zeroing y, clearing the mask) are fill
+    kernels, so a layer in that mode captures and replays like the default one: every
+    replay, with new inputs copied in and eager work between, agrees with the gather's
+    y to within the rounding bound of the atomic test above."""
+    w = wl.WORKLOADS["tiny"]
+    say("[case] graph capture, atomic combine")
+    ex = ExpertCache(w, 0)
+    blob = host_blob(w, ex).cuda()
+    h = make_handle(w)
+    xs = [torch.from_numpy(wl.layer_activations(w, l)).cuda() for l in (0, 1)]
+    lgs = [torch.from_numpy(wl.layer_logits(w, l)).cuda() for l in (0, 1)]
+    ref = []
+    for x, lg in zip(xs, lgs):
+        y = torch.empty(w.T, w.d, device="cuda")
+        mp.moe_prefill_run_layer(h, x, lg, y, weights=blob)
+        torch.cuda.synchronize()
+        ref.append(y.cpu().double())
+    x_s, lg_s = xs[0].clone(), lgs[0].clone()
+    y_s = torch.empty(w.T, w.d, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mp.moe_prefill_run_layer(h, x_s, lg_s, y_s, weights=blob, combine="atomic")
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="thread_local"):
+        mp.moe_prefill_run_layer(h, x_s, lg_s, y_s, weights=blob, combine="atomic")
+    for rep in range(2):
+        for i in (1, 0):
+            x_s.copy_(xs[i])
+            lg_s.copy_(lgs[i])
+            g.replay()
+            torch.cuda.synchronize()
+            diff = (y_s.cpu().double() - ref[i]).abs().max().item()
+            assert diff <= 1e-5 * ref[i].abs().max().item(), (rep, i, diff)
+            y_e = torch.empty_like(y_s)
+            mp.moe_prefill_run_layer(h, xs[i], lgs[i], y_e, weights=blob)
+            torch.cuda.synchronize()
+            assert torch.equal(y_e.cpu().double(), ref[i]), (rep, i, "eager")
+    del g
+    h.close()
+
+
 def test_atomic_combine_refuses_a_dm_export_and_unknown_modes():
     w = wl.WORKLOADS["tiny"]
     x = torch.from_numpy(wl.layer_activations(w, 0)).cuda()
