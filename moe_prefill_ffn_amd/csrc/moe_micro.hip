@@ -30,6 +30,10 @@
 //   overlap_scale_chain / overlap_scale_cvt  one scale-product MFMA chained through
 //                    its C operand (no wave waits for it) beside 64 fmas / converts
 //   mfma_f32_chain   two scale-product MFMAs chained through C, nothing else
+//   f8split_fma_mscale  an alternative block form, not the GEMMs': the exact block sums come
+//                    straight out as fp32 from two v_mfma_scale_f32_32x32x64_f8f6f4 (fp8
+//                    activation halves 16 * (x >> 4) and x & 15 in the two K halves, fp6
+//                    weights), then the scale MFMA and one fma per output (no convert)
 //   pipe_cvt_fma     cvt_fma_mscale with the epilogue one block behind the MFMAs
 //                    (the MFMAs of block b+1 issue before the VALU work of block b)
 //
@@ -51,6 +55,8 @@
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 namespace {
 
@@ -105,6 +111,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     v32f fzero;
 #pragma unroll
     for (int i = 0; i < 32; ++i) fzero[i] = 0.0f;
+    v16f fzero16;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) fzero16[i] = 0.0f;
     v16i m0 = zero, m1 = zero, m2 = zero, m3 = zero;
     v32f tp = fzero, t2 = fzero;
 
@@ -229,7 +238,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
             tp = tn;
             continue;
         }
-        if (kTest >= 5) {            // one VALU instruction kind alone: 64 independent ones per iteration
+        if (kTest >= 5 && kTest <= 7) {   // one VALU instruction kind alone: 64 independent ones per iteration
             float* f0 = acc0;
             float* f1 = acc1;
 #pragma unroll
@@ -250,6 +259,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
                     asm volatile("v_sub_f32 %0, %1, %2" : "=v"(dxr[i]) : "v"(m2[i]), "v"(dw));
                     asm volatile("v_sub_f32 %0, %1, %2" : "=v"(dxr[16 + i]) : "v"(m3[i]), "v"(dw));
                 }
+            }
+            continue;
+        }
+        if (kTest == 18) {           // an alternative block form: block sums straight to fp32
+            // (fp8 x fp6 MFMA over the split activation, K 64 per 32-block), scale MFMA, fma
+            touchf(dxv);
+            touchf(dw);
+            const v32f t = __builtin_amdgcn_mfma_f32_32x32x1f32(dxv, dw, fzero, 0, 0, 0);
+            const v8i a80 = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const v8i a81 = {a1.x, a1.y, a1.z, a1.w, a0.x, a0.y, a0.z, a0.w};
+            const v8i b8 = {b.x, b.y, b.z, b.w, b.x, b.y, 0, 0};
+            const int sa = (threadIdx.x & 63) < 32 ? 140 : 136;
+            const v16f f0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a80, b8, fzero16, 0, 3, 0, sa, 0, 127);
+            const v16f f1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a81, b8, fzero16, 0, 3, 0, sa, 0, 127);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                acc0[i] = __builtin_fmaf(f0[i], t[i], acc0[i]);
+                acc1[i] = __builtin_fmaf(f1[i], t[16 + i], acc1[i]);
             }
             continue;
         }
@@ -315,11 +342,11 @@ typedef struct moe_micro_result {
 // test: 0 mfma_i8, 1 cvt_fma_mscale, 2 cvt_fma_vscale, 3 sub_fma_vscale, 4 sub_fma_mscale,
 // 5 valu_fma, 6 valu_cvt, 7 valu_sub, 8 overlap_indep, 9 pipe_cvt_fma, 10 mfma_f32_scale,
 // 11 overlap_cvt, 12 overlap_fma16, 13 overlap_mul, 14 overlap_scale_fma, 15 overlap_scale_chain,
-// 16 overlap_scale_cvt, 17 mfma_f32_chain.  blocks_per_cu workgroups of 256 threads on each of
+// 16 overlap_scale_cvt, 17 mfma_f32_chain, 18 f8split_fma_mscale.  blocks_per_cu workgroups of 256 threads on each of
 // n_cu compute units.  Returns 0 or a negative HIP error.
 int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_per_cu, moe_micro_result_t* res)
 {
-    if (!res || iters < 1 || n_cu < 1 || blocks_per_cu < 1 || test < 0 || test > 17) return -1;
+    if (!res || iters < 1 || n_cu < 1 || blocks_per_cu < 1 || test < 0 || test > 18) return -1;
     MicroOut* d_out = nullptr;
     hipEvent_t e0, e1;
     if (hipMalloc(&d_out, sizeof(MicroOut)) != hipSuccess) return -2;
@@ -346,7 +373,8 @@ int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_pe
     case 14: hipLaunchKernelGGL(k_block<14>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     case 15: hipLaunchKernelGGL(k_block<15>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     case 16: hipLaunchKernelGGL(k_block<16>, grid, blk, 0, nullptr, iters, 3, d_out); break;
-    default: hipLaunchKernelGGL(k_block<17>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 17: hipLaunchKernelGGL(k_block<17>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    default: hipLaunchKernelGGL(k_block<18>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     }
     (void)hipEventRecord(e1, nullptr);
     hipError_t e = hipEventSynchronize(e1);

@@ -31,6 +31,7 @@ BLOCK_TESTS = {
     "overlap_scale_chain": 15,  # one scale-product MFMA chained through C beside 64 fmas
     "overlap_scale_cvt": 16,    # one scale-product MFMA chained through C beside 64 converts
     "mfma_f32_chain": 17,       # two scale-product MFMAs chained through C, nothing else
+    "f8split_fma_mscale": 18,   # alternative block form: fp8 x fp6 MFMAs give fp32 block sums, no convert
 }
 
 
