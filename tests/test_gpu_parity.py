@@ -415,6 +415,25 @@ def test_atomic_combine_captured_in_a_hip_graph():
     h.close()
 
 
+def test_noalloc_entry_point_with_the_atomic_combine():
+    """The allocation-free entry point takes the combine mode too: its y agrees with the
+    handle-based gather to within the rounding of a different add order."""
+    w = wl.WORKLOADS["tiny"]
+    say("[case] noalloc + atomic combine")
+    blob = host_blob(w, ExpertCache(w, 0)).cuda()
+    x = torch.from_numpy(wl.layer_activations(w, 0)).cuda()
+    lg = torch.from_numpy(wl.layer_logits(w, 0)).cuda()
+    h = make_handle(w)
+    y_ref = torch.empty(w.T, w.d, device="cuda")
+    mp.moe_prefill_run_layer(h, x, lg, y_ref, weights=blob)
+    y = torch.full((w.T, w.d), float("nan"), device="cuda")
+    mp.moe_prefill_run_layer_noalloc(w.d, w.f, w.E, w.k, x, lg, y, blob, combine="atomic")
+    torch.cuda.synchronize()
+    diff = (y.double() - y_ref.double()).abs().max().item()
+    assert diff <= 1e-5 * y_ref.abs().max().item(), diff
+    h.close()
+
+
 def test_atomic_combine_refuses_a_dm_export_and_unknown_modes():
     w = wl.WORKLOADS["tiny"]
     x = torch.from_numpy(wl.layer_activations(w, 0)).cuda()
