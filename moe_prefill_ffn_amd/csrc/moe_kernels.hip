@@ -538,7 +538,7 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
 // scales flag any scale outside that range; a launch that sees the flag takes
 // the plain unpack (kFold = false) and the exact unscaled arithmetic.  Both row
 // halves' integer MFMAs are issued before the first half's convert + fma, so the
-// second one runs under that VALU work; a wave stays at 123 VGPRs (four waves
+// second one runs under that VALU work; a wave stays within 124 VGPRs (four waves
 // per SIMD).  A partly filled half converts only the 8-row register groups that
 // hold rows of the tile.
 //
