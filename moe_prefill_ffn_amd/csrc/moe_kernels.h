@@ -15,7 +15,6 @@ struct GemmArgs {
     uint64_t q_off, s_off;    // matrix quant / scale section offsets in an expert
     const int32_t* tiles;     // [max_tiles][3]: expert, first row, end row
     const int32_t* ntiles;    // number of valid tiles (device)
-    const int32_t* order;     // tile order: heavy tiles first in each XCD range
     float* out;               // [R, N]; gate/up launch: GU, written only if not null
     int8_t* hq;               // gate/up launch: Hq [R, f] = Q8(SwiGLU(GU)) (else unused)
     float* dh;                // gate/up launch: its block scales [R][dh_stride]
@@ -49,7 +48,6 @@ struct LayerLaunch {
     int32_t* counts;
     int32_t* bounds;
     int32_t* tiles;
-    int32_t* tile_order;
     int32_t* ntiles;
     int32_t* rows;
     int32_t* pos;

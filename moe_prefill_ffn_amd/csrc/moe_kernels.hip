@@ -343,23 +343,20 @@ __global__ __launch_bounds__(256) void k_expert_load(const uint8_t* __restrict__
 // workgroup 0 also writes the bounds and the GEMM row-tile list (expert, first
 // row, end row; kBM rows per tile; expert order) for the kernels that follow, a
 // run of consecutive tiles per thread (the run's expert found by binary search
-// over the experts' first tiles: empty experts own no tiles), and the last
-// workgroup the order in which the GEMM launches take the tiles.
+// over the experts' first tiles: empty experts own no tiles).
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eidx, int64_t R, int k,
                                                  const uint32_t* __restrict__ mask,
                                                  const int32_t* __restrict__ wprefix,
                                                  const int32_t* __restrict__ counts, int E, int W,
                                                  int32_t* __restrict__ bounds,
                                                  int32_t* __restrict__ tiles,
-                                                 int32_t* __restrict__ tile_order,
                                                  int32_t* __restrict__ ntiles,
                                                  int32_t* __restrict__ rows, int32_t* __restrict__ pos,
                                                  int32_t* __restrict__ rtok)
 {
     __shared__ int s_bounds[kRouteMaxE];
     __shared__ int s_tfirst[kRouteMaxE + 1];              // first tile of each expert (writer)
-    __shared__ int s_wc[4], s_wt[4], s_wh[4];
-    __shared__ int s_hstart[9];                           // heavy tiles before each XCD range
+    __shared__ int s_wc[4], s_wt[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool writer = blockIdx.x == 0;
     int c4[4], t4[4], sc = 0, st = 0;
@@ -414,7 +411,7 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
     __syncthreads();
     // tile tau belongs to the expert e with s_tfirst[e] <= tau < s_tfirst[e + 1]; each
     // thread takes a run of consecutive tiles (a binary search for the run's first
-    // tile, then a walk).  Tiles of more than 32 rows are "heavy".
+    // tile, then a walk).
     const int run = (all_t + 255) >> 8;
     const int t0 = tid * run, t1 = t0 + run < all_t ? t0 + run : all_t;
     int lo0 = 0;
@@ -441,55 +438,6 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
             tiles[3 * tau + 0] = lo;
             tiles[3 * tau + 1] = r0;
             tiles[3 * tau + 2] = r1;
-        }
-    }
-    if (blockIdx.x == gridDim.x - 1) {
-        // GEMM tile order (the last workgroup, beside the writer): the tiles are
-        // split over the 8 XCDs in contiguous ranges, as the GEMMs split them; inside
-        // each range the heavy tiles come first, both kinds in tile order.
-        int lo = lo0, r0, r1, nheavy = 0;
-        for (int tau = t0; tau < t1; ++tau) {
-            tile_rows(tau, lo, r0, r1);
-            nheavy += r1 - r0 > kBM / 2;
-        }
-        int hincl = nheavy;                               // heavy tiles up to this run's end
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(hincl, o);
-            if (lane >= o) hincl += y;
-        }
-        if (lane == 63) s_wh[wave] = hincl;
-        const int tq = all_t >> 3, tr = all_t & 7;
-        auto range_start = [&](int x) { return x * tq + (x < tr ? x : tr); };
-        __syncthreads();
-        int hb = hincl - nheavy, htot = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            hb += i < wave ? s_wh[i] : 0;
-            htot += s_wh[i];
-        }
-        if (tid <= 8) s_hstart[tid] = htot;               // ranges that start at all_t
-        __syncthreads();
-        lo = lo0;
-        int h = hb;
-        for (int tau = t0; tau < t1; ++tau) {             // heavy tiles before each range start
-            for (int x = 0; x < 8; ++x)
-                if (range_start(x) == tau) s_hstart[x] = h;
-            tile_rows(tau, lo, r0, r1);
-            h += r1 - r0 > kBM / 2;
-        }
-        __syncthreads();
-        lo = lo0;
-        h = hb;
-        for (int tau = t0; tau < t1; ++tau) {
-            int x = 7;
-            while (range_start(x) > tau) --x;              // the range holding tau
-            tile_rows(tau, lo, r0, r1);
-            const bool heavy = r1 - r0 > kBM / 2;
-            const int ta = range_start(x), hx = h - s_hstart[x];
-            const int nh = s_hstart[x + 1] - s_hstart[x];
-            tile_order[heavy ? ta + hx : ta + nh + (tau - ta - hx)] = tau;
-            h += heavy;
         }
     }
     const int64_t p = (int64_t)blockIdx.x * 256 + tid;
@@ -545,8 +493,8 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ eid
 // Workgroups are numbered so that each XCD (dispatch is round-robin over the
 // 8 XCDs) receives a contiguous run of row tiles with all their n-groups: the
 // n-groups of a row tile and the row tiles of an expert share that XCD's L2.
-// Inside an XCD's run both launches take the tiles of more than 32 rows first,
-// so the workgroups that start last are the cheaper half-height ones.
+// Inside an XCD's run the tiles go in tile order, so an expert's tiles (a full
+// one and its partial last one) run together and read its weights once.
 constexpr int kGemmThreads = 256;         // 4 waves
 constexpr int kRing = 4;                  // LDS stages = stages per scale group
 constexpr int kA_OFF = 0;                 // [64 rows][4 chunks of 16 B], chunks swizzled per row
@@ -681,7 +629,7 @@ struct GemmItem {
 };
 
 // XCD x (dispatch is round-robin over the 8 XCDs) takes a contiguous range of row
-// tiles, all their n-groups, the tiles of more than 32 rows first.  Inside the range
+// tiles with all their n-groups, in tile order.  Inside the range
 // the workgroups go by super-groups of kSuperNG n-groups: all the range's tiles of
 // n-groups 0-7, then of 8-15, ...  The workgroups an XCD runs at once then share
 // each weight slice among many tiles and each tile's activation rows among 8
@@ -713,8 +661,7 @@ __device__ __forceinline__ bool gemm_item(const GemmArgs& g, GemmItem& it)
             k = rem / part;
             ng = full * kSuperNG + rem % part;
         }
-        const int o = g.order[ta + k];                    // heavy tiles first in each range
-        tile = o < 0 ? 0 : (o >= nt_all ? nt_all - 1 : o);   // a no-op for a sound order
+        tile = ta + k;                                    // the range's tiles in tile order
     }
     const int te = g.tiles[3 * tile + 0];
     it.ng = ng;
@@ -1088,7 +1035,7 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
                            L.E, L.expert_stride, L.load_stats);
     mark(L, kScatter, st);
     hipLaunchKernelGGL(k_scatter, dim3(nblk(R, 256)), dim3(256), 0, st, L.eidx, R, L.k, L.mask,
-                       L.wprefix, L.counts, L.E, L.W, L.bounds, L.tiles, L.tile_order, L.ntiles, L.rows, L.pos,
+                       L.wprefix, L.counts, L.E, L.W, L.bounds, L.tiles, L.ntiles, L.rows, L.pos,
                        L.rtok);
     const int max_tiles_now = (int)((R + kBM - 1) / kBM) + (L.E < R ? L.E : (int)R);
 
@@ -1102,7 +1049,6 @@ hipError_t launch_layer(const LayerLaunch& L, hipStream_t st)
     gu.q_off = L.gu_q_off;
     gu.s_off = L.gu_s_off;
     gu.tiles = L.tiles;
-    gu.order = L.tile_order;                              // the down launch keeps it
     gu.ntiles = L.ntiles;
     gu.out = L.gu;
     gu.hq = L.hq;

@@ -86,7 +86,7 @@ constexpr int kScaleFlagWords = 2;
 MOE_HD static inline uint64_t mask_words(int E, int W) { return (uint64_t)E * W + kScaleFlagWords; }
 
 struct WsLayout {
-    uint64_t eidx, wts, mask, wprefix, counts, bounds, tiles, tile_order, ntiles, load_stats;
+    uint64_t eidx, wts, mask, wprefix, counts, bounds, tiles, ntiles, load_stats;
     uint64_t rows, pos, rtok, xq, dx, hq, dh, dm;
     uint64_t total;
     int W;            // 32-token words per expert in the membership mask
@@ -108,7 +108,6 @@ static inline WsLayout ws_layout(int d, int f, int E, int k, int Tmax)
     L.counts = take((uint64_t)E * 4);
     L.bounds = take((uint64_t)(E + 1) * 4);
     L.tiles = take((uint64_t)L.max_tiles * 3 * 4);
-    L.tile_order = take((uint64_t)L.max_tiles * 4);
     L.ntiles = take(4);
     L.load_stats = take(16);                              // experts, bytes of active-expert loads
     L.rows = take(R * 4);

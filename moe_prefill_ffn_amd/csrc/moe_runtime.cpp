@@ -253,7 +253,6 @@ void bind_layer(LayerLaunch& LL, uint8_t* w, const WsLayout& L, const BlobLayout
     LL.counts = reinterpret_cast<int32_t*>(w + L.counts);
     LL.bounds = reinterpret_cast<int32_t*>(w + L.bounds);
     LL.tiles = reinterpret_cast<int32_t*>(w + L.tiles);
-    LL.tile_order = reinterpret_cast<int32_t*>(w + L.tile_order);
     LL.ntiles = reinterpret_cast<int32_t*>(w + L.ntiles);
     LL.rows = reinterpret_cast<int32_t*>(w + L.rows);
     LL.pos = reinterpret_cast<int32_t*>(w + L.pos);
