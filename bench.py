@@ -577,7 +577,7 @@ def micro_leg(torch, dev) -> dict:
     forms = {}
     for name, iters in (("mfma_i8", 40000), ("cvt_fma_mscale", 20000), ("cvt_fma_vscale", 20000),
                         ("sub_fma_vscale", 20000), ("sub_fma_mscale", 20000), ("pipe_cvt_fma", 20000),
-                        ("overlap_indep", 20000), ("f8split_fma_mscale", 20000)):
+                        ("overlap_indep", 20000), ("f8split_fma_mscale", 20000), ("f6split_fma_mscale", 20000)):
         for wps in (4, 2):
             r = micro.block(name, iters, n_cu, wps)
             macs_iter = (4 if name == "mfma_i8" else 2) * 32768
@@ -591,10 +591,10 @@ def micro_leg(torch, dev) -> dict:
             }
     out["block_forms"] = forms
     out["int8_mfma_peak_TOPS_measured"] = forms["mfma_i8@4w"]["TOPS"]
-    # the ceiling of the arithmetic the GEMMs run (int8 MFMA block sums); the fp8 x fp6 split
-    # form is an alternative design, reported beside it
+    # the ceiling of the arithmetic the GEMMs run (int8 MFMA block sums); the fp8 x fp6 and
+    # fp6 x fp6 split forms are alternative designs, reported beside it
     best = max((v["TOPS"], k) for k, v in forms.items()
-               if not k.startswith(("mfma_i8", "overlap_indep", "f8split")))
+               if not k.startswith(("mfma_i8", "overlap_indep", "f8split", "f6split")))
     out["epilogue_ceiling_TOPS"] = best[0]
     out["epilogue_ceiling_form"] = best[1]
     valu = {}
@@ -617,6 +617,14 @@ def micro_leg(torch, dev) -> dict:
             row[name] = round(simd_cycles(r, 20000), 1)
         coexec[f"{wps}w"] = row
     out["coexec_simd_cycles_per_iter"] = coexec
+    # matrix-core cycles per instruction with four waves per SIMD (four per wave and iteration):
+    # int8 32x32x32 against fp6 x fp6 32x32x64
+    rates = {}
+    for name, key in (("mfma_i8", "i8_32x32x32"), ("mfma_f6", "f6_32x32x64")):
+        iters = 20000
+        r = micro.block(name, iters, n_cu, 4)
+        rates[key] = round(simd_cycles(r, iters) / (4 * 4), 2)
+    out["mfma_cycles_per_instr"] = rates
     iters = 20000
     r = micro.block("mfma_f32_scale", iters, n_cu, 4)
     # SIMD cycles per scale-product MFMA (4 waves per SIMD, 2 per iteration) and products/s

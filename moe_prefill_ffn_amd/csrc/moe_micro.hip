@@ -34,6 +34,11 @@
 //                    straight out as fp32 from two v_mfma_scale_f32_32x32x64_f8f6f4 (fp8
 //                    activation halves 16 * (x >> 4) and x & 15 in the two K halves, fp6
 //                    weights), then the scale MFMA and one fma per output (no convert)
+//   mfma_f6          fp6 x fp6 MFMAs alone (v_mfma_scale_f32_32x32x64_f8f6f4, E3M2 both sides):
+//                    the rate of the matrix cores on fp6 operands
+//   f6split_fma_mscale  a third block form: the activation split as 16 hi + lo with hi in
+//                    [-8, 8] and lo in [-8, 7], both halves and the weights in fp6 E3M2, so the
+//                    fp6 MFMA (twice the fp8 rate) returns the exact block sums as fp32
 //   pipe_cvt_fma     cvt_fma_mscale with the epilogue one block behind the MFMAs
 //                    (the MFMAs of block b+1 issue before the VALU work of block b)
 //
@@ -115,6 +120,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
     for (int i = 0; i < 16; ++i) fzero16[i] = 0.0f;
     v16i m0 = zero, m1 = zero, m2 = zero, m3 = zero;
+    v16f c60 = fzero16, c61 = fzero16, c62 = fzero16, c63 = fzero16;
     v32f tp = fzero, t2 = fzero;
 
     __syncthreads();
@@ -262,6 +268,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
             }
             continue;
         }
+        if (kTest == 19) {           // fp6 x fp6 MFMAs alone (E3M2 both sides, K 64): four chains
+            const v8i a6 = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, 0, 0};
+            const v8i b6 = {b.x, b.y, b.z, b.w, a1.z, a1.w, 0, 0};
+            c60 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a6, b6, c60, 3, 3, 0, 127, 0, 127);
+            c61 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b6, a6, c61, 3, 3, 0, 127, 0, 127);
+            c62 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a6, a6, c62, 3, 3, 0, 127, 0, 127);
+            c63 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b6, b6, c63, 3, 3, 0, 127, 0, 127);
+            continue;
+        }
+        if (kTest == 20) {           // another alternative block form: the split activation
+            // 16 hi + lo with hi in [-8, 8] and lo in [-8, 7] goes into the two K halves as
+            // fp6 E3M2 (exact: codes 0..8 are 0..8 / 16), the weights as fp6 E3M2 too; the
+            // E8M0 block scales (2^8 and 2^4 for the halves, 2^4 for the weights) make the
+            // MFMA return the exact block sum in fp32; then the scale MFMA and one fma per output
+            touchf(dxv);
+            touchf(dw);
+            const v32f t = __builtin_amdgcn_mfma_f32_32x32x1f32(dxv, dw, fzero, 0, 0, 0);
+            const v8i a60 = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, 0, 0};
+            const v8i a61 = {a1.x, a1.y, a1.z, a1.w, a0.x, a0.y, 0, 0};
+            const v8i b6 = {b.x, b.y, b.z, b.w, a1.z, a1.w, 0, 0};
+            const int sa = (threadIdx.x & 63) < 32 ? 135 : 131;
+            const v16f f0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a60, b6, fzero16, 3, 3, 0, sa, 0, 131);
+            const v16f f1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a61, b6, fzero16, 3, 3, 0, sa, 0, 131);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                acc0[i] = __builtin_fmaf(f0[i], t[i], acc0[i]);
+                acc1[i] = __builtin_fmaf(f1[i], t[16 + i], acc1[i]);
+            }
+            continue;
+        }
         if (kTest == 18) {           // an alternative block form: block sums straight to fp32
             // (fp8 x fp6 MFMA over the split activation, K 64 per 32-block), scale MFMA, fma
             touchf(dxv);
@@ -304,7 +340,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     }
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s += acc0[i] + acc1[i] + (float)(m0[i] + m1[i] + m2[i] + m3[i]) + tp[i] + t2[i];
+    for (int i = 0; i < 16; ++i)
+        s += acc0[i] + acc1[i] + (float)(m0[i] + m1[i] + m2[i] + m3[i]) + tp[i] + t2[i] + c60[i] + c61[i] + c62[i] + c63[i];
     record(out, c0, r0, s);
 }
 
@@ -342,11 +379,12 @@ typedef struct moe_micro_result {
 // test: 0 mfma_i8, 1 cvt_fma_mscale, 2 cvt_fma_vscale, 3 sub_fma_vscale, 4 sub_fma_mscale,
 // 5 valu_fma, 6 valu_cvt, 7 valu_sub, 8 overlap_indep, 9 pipe_cvt_fma, 10 mfma_f32_scale,
 // 11 overlap_cvt, 12 overlap_fma16, 13 overlap_mul, 14 overlap_scale_fma, 15 overlap_scale_chain,
-// 16 overlap_scale_cvt, 17 mfma_f32_chain, 18 f8split_fma_mscale.  blocks_per_cu workgroups of 256 threads on each of
+// 16 overlap_scale_cvt, 17 mfma_f32_chain, 18 f8split_fma_mscale, 19 mfma_f6, 20 f6split_fma_mscale.
+// blocks_per_cu workgroups of 256 threads on each of
 // n_cu compute units.  Returns 0 or a negative HIP error.
 int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_per_cu, moe_micro_result_t* res)
 {
-    if (!res || iters < 1 || n_cu < 1 || blocks_per_cu < 1 || test < 0 || test > 18) return -1;
+    if (!res || iters < 1 || n_cu < 1 || blocks_per_cu < 1 || test < 0 || test > 20) return -1;
     MicroOut* d_out = nullptr;
     hipEvent_t e0, e1;
     if (hipMalloc(&d_out, sizeof(MicroOut)) != hipSuccess) return -2;
@@ -374,7 +412,9 @@ int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_pe
     case 15: hipLaunchKernelGGL(k_block<15>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     case 16: hipLaunchKernelGGL(k_block<16>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     case 17: hipLaunchKernelGGL(k_block<17>, grid, blk, 0, nullptr, iters, 3, d_out); break;
-    default: hipLaunchKernelGGL(k_block<18>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 18: hipLaunchKernelGGL(k_block<18>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    case 19: hipLaunchKernelGGL(k_block<19>, grid, blk, 0, nullptr, iters, 3, d_out); break;
+    default: hipLaunchKernelGGL(k_block<20>, grid, blk, 0, nullptr, iters, 3, d_out); break;
     }
     (void)hipEventRecord(e1, nullptr);
     hipError_t e = hipEventSynchronize(e1);
@@ -392,7 +432,9 @@ int moe_micro_block(int32_t test, int32_t iters, int32_t n_cu, int32_t blocks_pe
     res->clock_ghz = h.rt ? (double)h.cycles / ((double)h.rt / 100e6) / 1e9 : 0.0;
     // MFMA tests: int8 MACs per iteration per wave (x2 ops); the scale-product tests count
     // their fp32 products (2048 per MFMA); the VALU-only tests count none
+    // (mfma_f6: its own K-64 MACs, four MFMAs per iteration)
     const double macs = test == 0 ? 4.0 * 32768.0
+                      : test == 19 ? 4.0 * 65536.0
                       : test == 10 ? 2.0 * 2048.0
                       : (test == 14 || test == 15 || test == 16) ? 2048.0
                       : test == 17 ? 2.0 * 2048.0

@@ -32,6 +32,8 @@ BLOCK_TESTS = {
     "overlap_scale_cvt": 16,    # one scale-product MFMA chained through C beside 64 converts
     "mfma_f32_chain": 17,       # two scale-product MFMAs chained through C, nothing else
     "f8split_fma_mscale": 18,   # alternative block form: fp8 x fp6 MFMAs give fp32 block sums, no convert
+    "mfma_f6": 19,              # fp6 x fp6 MFMAs alone (four chains, K 64 each)
+    "f6split_fma_mscale": 20,   # alternative block form: fp6 x fp6 MFMAs give fp32 block sums, no convert
 }
 
 
