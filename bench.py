@@ -664,8 +664,9 @@ def main() -> int:
     ap.add_argument("--headline-only", action="store_true",
                     help="only the headline layer (no denominators, no T=1024 layer, no streaming, no CPU "
                          "baseline): the command the kernel-trace and counter profiles run")
-    ap.add_argument("--workload", default="skew", choices=("skew", "resident"),
-                    help="with --headline-only: the layer to run (the T=1024 layer for its own profiles)")
+    ap.add_argument("--workload", default="skew", choices=("skew", "resident", "stream48"),
+                    help="with --headline-only: the layer to run (the T=1024 layer, or a resident layer of "
+                         "the 48-layer stack's shape, for their own profiles)")
     ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--no-active", action="store_true", help="skip the active-expert streaming comparison")
     ap.add_argument("--no-cpu", action="store_true")
