@@ -658,7 +658,7 @@ def main() -> int:
                     help="untimed layers first: the MI355X needs ~40 ms of sustained work to reach "
                          "its steady clocks (a cold layer takes ~290 us, a warm one ~195 us)")
     ap.add_argument("--stream-passes", type=int, default=3)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target CPU time of the oracle baseline's token sample")
     ap.add_argument("--no-micro", action="store_true", help="skip the microbenchmark denominators")
     ap.add_argument("--headline-only", action="store_true",
